@@ -1,0 +1,129 @@
+/*
+ * dq4.h -- C ABI of the MI355X (gfx950) nested 4-bit dequantization library.
+ *
+ * The operation (bitsandbytes issue "Fuse nested scale reconstruction into
+ * SM103 4-bit dequantization", section "Proposed experiment"): for every
+ * element i of a flat row-major tensor of packed 4-bit codes
+ *
+ *     b     = i / blocksize                 outer block
+ *     g     = b / nested_blocksize          nested group, counted in outer blocks
+ *     t     = fl32(scale_codebook[scale_codes[b]] * nested_absmax[g])
+ *     s     = fl32(t + offset)              rounded separately: no fused multiply-add
+ *     k     = nibble of element i           byte i/2; low nibble for even i, high for odd i
+ *     out_i = cvt(fl32(codebook4[k] * s))   cvt: identity (F32) or IEEE
+ *                                           round-to-nearest-even to F16 / BF16,
+ *                                           subnormals kept
+ *
+ * fl32() is one IEEE binary32 round-to-nearest-even step.  The section
+ * "Correctness requirements" of that issue fixes the separate rounding of the
+ * multiply and the add, and requires the result to be bitwise identical to the
+ * three-step sequence of its section "Problem" (scale codes to an FP32 buffer,
+ * a separate offset add, then the value pass).  The per-block scale is rebuilt
+ * in registers inside the value pass: no FP32 scale tensor is written.
+ *
+ * Buffers (all of them caller-owned; device memory unless stated otherwise):
+ *   packed          ceil(n/2) bytes.  For odd n the high nibble of the last
+ *                   byte is read and ignored.
+ *   scale_codes     ceil(n/blocksize) bytes, one uint8 code per outer block.
+ *   nested_absmax   ceil(ceil(n/blocksize)/nested_blocksize) FP32 values.
+ *   scale_codebook  256 FP32 values (indexed by the scale code).
+ *   codebook4       16 FP32 values (the NF4 or FP4 decode table, indexed by
+ *                   the 4-bit code; any 16 values are accepted).
+ *   offset          host FP32 scalar, passed by value.
+ *   out             n elements of the output type, densely packed.
+ * No pointer has to be aligned; 4-byte aligned `packed` and 16-byte aligned
+ * `out` with element windows starting at a multiple of 8 take the vectorised
+ * path, anything else a per-element path with bitwise identical results.
+ * Input and output ranges must not overlap.
+ *
+ * Ownership and ordering: the library allocates nothing, frees nothing, keeps
+ * no handle to any buffer and never synchronizes.  Each call enqueues exactly
+ * one kernel on `stream` (a hipStream_t; NULL means the legacy default
+ * stream) and returns; the output is ready when that stream reaches the
+ * kernel.  Calls are reentrant and thread-safe.
+ *
+ * Errors: validation happens on the host before anything is enqueued.  A call
+ * that returns anything but DQ4_OK has enqueued nothing and left `out`
+ * untouched, except DQ4_EHIP, which reports that the launch itself failed
+ * (the HIP error code is kept, per thread, for dq4_last_hip_error()).
+ */
+#ifndef DQ4_H
+#define DQ4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dq4_status_t;
+
+enum {
+    DQ4_OK = 0,
+    DQ4_EINVAL = 1,        /* null pointer with work to do, negative size, bad
+                              row window, unknown output type */
+    DQ4_EUNSUPPORTED = 2,  /* blocksize not a power of two in [32, 4096], or
+                              nested_blocksize other than 256 */
+    DQ4_EHIP = 3           /* the kernel launch failed */
+};
+
+enum {
+    DQ4_F32 = 0,
+    DQ4_F16 = 1,
+    DQ4_BF16 = 2
+};
+
+/*
+ * Whole-tensor dequantization of n elements (the fused nested dequantization
+ * of the bitsandbytes issue above, section "Proposed experiment").
+ *
+ * blocksize: outer block size, a power of two from 32 to 4096 (section
+ *   "Correctness requirements": block sizes 32 through 4096).
+ * nested_blocksize: outer blocks per nested absmax; 256 is the only nested
+ *   layout supported (section "Proposed experiment", the routing guard
+ *   state2.blocksize == 256).
+ * out_dtype: DQ4_F32, DQ4_F16 or DQ4_BF16.
+ * n == 0 is a no-op that returns DQ4_OK without touching the GPU.
+ */
+dq4_status_t dq4_nested_dequant(const uint8_t *packed, const uint8_t *scale_codes,
+                                const float *nested_absmax, const float *scale_codebook,
+                                const float *codebook4, float offset, int64_t n,
+                                int32_t blocksize, int32_t nested_blocksize,
+                                int32_t out_dtype, void *out, void *stream);
+
+/*
+ * Row-window dequantization (llama.cpp PR "cuda: out_prod dequantizes a 2D
+ * weight in row blocks", section "What" and the review): rows [r0, r0 + rows)
+ * of an n_rows x n_cols row-major weight, so a large weight can stream through
+ * one bounded output buffer.  Output element (r - r0) * n_cols + j is global
+ * element r * n_cols + j of the whole-tensor call; block and group indices
+ * come from the global element index, and the metadata pointers are those of
+ * the whole tensor.  `out` holds rows * n_cols elements.
+ * Requires 0 <= r0, 0 <= rows, r0 + rows <= n_rows; rows == 0 is a no-op.
+ */
+dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale_codes,
+                                     const float *nested_absmax,
+                                     const float *scale_codebook, const float *codebook4,
+                                     float offset, int64_t n_rows, int64_t n_cols,
+                                     int64_t r0, int64_t rows, int32_t blocksize,
+                                     int32_t nested_blocksize, int32_t out_dtype, void *out,
+                                     void *stream);
+
+/*
+ * Rows per transient block (llama.cpp PR above, review): the largest row count
+ * whose rows * n_cols * elem_bytes fits in budget_bytes, and at least 1.
+ * Non-positive arguments return 1.  Host only.
+ */
+int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *dq4_status_string(dq4_status_t status);
+
+/* HIP error code of this thread's last DQ4_EHIP, 0 if none. */
+int32_t dq4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ4_H */
