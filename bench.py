@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark: nested NF4 -> FP16 dequantization of a 28672 x 8192 weight, bs 64.
+
+One step is one call of dq4_nested_dequant over the whole tensor (235 M
+elements): element -> block -> group indexing, metadata fetch, in-register
+scale reconstruction, 4-bit decode and FP16 conversion and store, all in one
+kernel.  Inputs are resident in HBM before the timed region starts.  Several
+independent input/output buffer sets are cycled so repeated steps cannot be
+served from the 256 MB last-level cache.
+
+Prints ONE JSON line (rank 0, one GPU):
+  value      = algorithmic bytes per step / wall-clock time per step, in GB/s
+  roofline   = the kernel's achieved bandwidth from HIP events on its stream
+               against MI355X's 8 TB/s HBM peak, and the HBM traffic measured
+               by rocprofv3 counters (profiles/), when they match this source
+  cpu_baseline = the CPU oracle (single thread) on the same inputs
+Timing protocol after the bitsandbytes issue's evidence plan ("B300 evidence
+plan"): >= 20 warmups, 7 timed batches of inner launches, every batch sample
+reported with median, p10 and p90.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dequantized GB/s (fraction of HBM peak), NF4→FP16 28672×8192 bs64"
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "dq4_vec_kernel_f16_28672x8192_bs64_pmc.json")
+KERNEL_SOURCE = os.path.join(ROOT, "block_wise_bit_amd", "csrc", "dq4.hip")
+
+
+def algorithmic_bytes(n: int, blocksize: int, out_bytes: int, nested: int = 256) -> int:
+    """Bytes the method must move once: packed nibbles, codes, absmax, codebooks, output."""
+    nb = -(-n // blocksize)
+    ng = -(-nb // nested)
+    return (n + 1) // 2 + nb + 4 * ng + 4 * (256 + 16) + out_bytes * n
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(PMC_SUMMARY) as fh:
+            s = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * q
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def copy_calibration(args, torch) -> int:
+    """A plain copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel over
+    its true bytes give the scale factors of the HBM byte counters."""
+    nbytes = args.copy_calibration << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "us_per_copy": round(us, 3),
+                      "GBps": round(2 * nbytes / (us * 1e-6) / 1e9, 2)}), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=700, help="timed steps (split into 7 batches)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled")
+    ap.add_argument("--batches", type=int, default=7)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline (whole-tensor passes)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, time a plain device-to-device copy of MIB "
+                         "MiB (the reference kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); the "
+              "dequantization shards without any exchange, so there is no multi-GPU step to time.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_wise_bit_amd as dq4
+    from block_wise_bit_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        return copy_calibration(args, torch)
+    dq4.library()  # fail loudly if the HIP library is missing
+
+    wl = inputs.HEADLINE
+    n, bs = wl.n, wl.blocksize
+    out_bytes = 2
+    alg_bytes = algorithmic_bytes(n, bs, out_bytes)
+    print(f"[bench] workload {wl.name}: n={n} bs={bs} algorithmic bytes/step={alg_bytes}",
+          file=sys.stderr, flush=True)
+
+    x = wl.inputs()
+    sets = []
+    for r in range(max(1, args.rotate)):
+        dev = dq4.to_device(x, "cuda:0")
+        out = torch.empty(n, dtype=torch.float16, device="cuda:0")
+        sets.append((dev, out))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    offset = float(x.offset)
+
+    def step(k):
+        dev, out = sets[k % len(sets)]
+        dq4.dq4_nested_dequant(**dev, offset=offset, n=n, blocksize=bs, out_dtype=torch.float16,
+                               out=out, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.warmup} warmup steps done", file=sys.stderr, flush=True)
+
+    # timed region: K steps in `batches` batches, one event pair per batch on
+    # the launch stream, wall clock around the whole region
+    K = args.steps
+    nbatch = max(1, min(args.batches, K))
+    per = [K // nbatch + (1 if i < K % nbatch else 0) for i in range(nbatch)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nbatch)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    k = 0
+    for (e0, e1), m in zip(evs, per):
+        e0.record(stream)
+        for _ in range(m):
+            step(k)
+            k += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    batch_us = [e0.elapsed_time(e1) * 1e3 / m for (e0, e1), m in zip(evs, per)]
+    kernel_us = sum(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs) / K
+    ms_per_step = wall * 1e3 / K
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
+    print(f"[bench] {K} timed steps: {ms_per_step * 1e3:.2f} us/step wall, "
+          f"{kernel_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
+
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_rows": wl.n_rows, "n_cols": wl.n_cols,
+                   "format": wl.fmt, "out_dtype": "f16", "blocksize": bs,
+                   "nested_blocksize": 256, "offset": wl.offset, "seed": wl.seed,
+                   "buffer_sets": len(sets), "input_digest": x.digest()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "elements_per_s": round(n / (kernel_us * 1e-6), 1),
+        "kernel_us": {"mean": round(kernel_us, 3), "batches": [round(b, 3) for b in batch_us],
+                      "median": round(percentile(batch_us, 0.5), 3),
+                      "p10": round(percentile(batch_us, 0.1), 3),
+                      "p90": round(percentile(batch_us, 0.9), 3)},
+        "kernel_source_sha256_16": kernel_source_digest(),
+        "device": torch.cuda.get_device_name(0),
+        "cpu_baseline": None,
+        "parity": None,
+    }
+
+    if not args.no_cpu:
+        import oracle
+
+        got = sets[(K - 1) % len(sets)][1].cpu().view(torch.int16).numpy().view(np.uint16)
+        passes, t_cpu, want = 0, 0.0, None
+        while passes < 3 and (passes == 0 or t_cpu < args.cpu_seconds):
+            c0 = time.perf_counter()
+            want = oracle.dequant(x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook,
+                                  x.codebook4, x.offset, n, bs, out_dtype="f16")
+            t_cpu += time.perf_counter() - c0
+            passes += 1
+            print(f"[bench] oracle pass {passes}: {t_cpu:.2f} s so far", file=sys.stderr,
+                  flush=True)
+        mismatches = int(np.count_nonzero(got != want))
+        cpu_gbs = alg_bytes * passes / t_cpu / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {wl.n_rows}x{wl.n_cols} tensor, {passes} single-threaded "
+                      f"pass(es), {t_cpu:.2f} s; host {platform.processor() or platform.machine()}"
+                      f" with {os.cpu_count()} logical cpus",
+            "elements_per_s": round(n * passes / t_cpu, 1)}
+        result["parity"] = {"compared_elements": n, "mismatches": mismatches,
+                            "bit_exact": mismatches == 0}
+
+    print(json.dumps(result), flush=True)
+    if result["parity"] is not None and not result["parity"]["bit_exact"]:
+        return 3
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,230 @@
+"""MI355X (gfx950) nested block-wise 4-bit dequantization.
+
+Thin Python binding of the C ABI in include/dq4.h (libdq4.so, built in-tree
+by block_wise_bit_amd/build.py).  The functions keep the C names; they only
+check and marshal arguments -- every step of the dequantization runs in the
+HIP kernels of the library.  torch provides device memory and the current
+stream, nothing else.  There is no fallback: if the library is missing or
+cannot be loaded, every call raises.
+
+    dq4_nested_dequant(packed, scale_codes, nested_absmax, scale_codebook,
+                       codebook4, offset, n, blocksize, ...) -> tensor
+    dq4_nested_dequant_rows(..., n_rows, n_cols, r0, rows, ...) -> tensor
+    dq4_rows_per_block(n_cols, elem_bytes, budget_bytes) -> int
+    dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(PKG_DIR, "libdq4.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "dq4.h")
+
+DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP = 0, 1, 2, 3
+DQ4_F32, DQ4_F16, DQ4_BF16 = 0, 1, 2
+NESTED_BLOCKSIZE = 256
+ROW_BLOCK_BUDGET_BYTES = 256 << 20   # 256 MiB of F32 per transient row block
+
+_lib = None
+
+
+class Dq4Error(RuntimeError):
+    """A launch failure reported by the library (DQ4_EHIP)."""
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libdq4.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(
+            f"{LIBRARY_PATH} is missing: build it with `python -m block_wise_bit_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    P = ctypes.c_void_p
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    lib.dq4_nested_dequant.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32, P, P]
+    lib.dq4_nested_dequant.restype = i32
+    lib.dq4_nested_dequant_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i64, i64, i32, i32,
+                                            i32, P, P]
+    lib.dq4_nested_dequant_rows.restype = i32
+    lib.dq4_rows_per_block.argtypes = [i64, i64, i64]
+    lib.dq4_rows_per_block.restype = i64
+    lib.dq4_status_string.argtypes = [i32]
+    lib.dq4_status_string.restype = ctypes.c_char_p
+    lib.dq4_last_hip_error.argtypes = []
+    lib.dq4_last_hip_error.restype = i32
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> List[str]:
+    """Names of the functions include/dq4.h declares."""
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(dq4_[a-z0-9_]+)\s*\(", text)
+
+
+# ----------------------------------------------------------------------------
+# plain C entry points
+# ----------------------------------------------------------------------------
+def dq4_status_string(status: int) -> str:
+    return library().dq4_status_string(int(status)).decode()
+
+
+def dq4_last_hip_error() -> int:
+    return int(library().dq4_last_hip_error())
+
+
+def dq4_rows_per_block(n_cols: int, elem_bytes: int = 4,
+                       budget_bytes: int = ROW_BLOCK_BUDGET_BYTES) -> int:
+    return int(library().dq4_rows_per_block(int(n_cols), int(elem_bytes), int(budget_bytes)))
+
+
+def dq4_row_windows(n_rows: int, n_cols: int, elem_bytes: int = 4,
+                    budget_bytes: int = ROW_BLOCK_BUDGET_BYTES) -> List[Tuple[int, int]]:
+    """Consecutive row windows (r0, rows) of at most dq4_rows_per_block rows."""
+    rpb = dq4_rows_per_block(n_cols, elem_bytes, budget_bytes)
+    return [(r0, min(rpb, n_rows - r0)) for r0 in range(0, n_rows, rpb)]
+
+
+def _raise_for(status: int, what: str) -> None:
+    if status == DQ4_OK:
+        return
+    msg = f"{what}: {dq4_status_string(status)}"
+    if status == DQ4_EHIP:
+        raise Dq4Error(f"{msg} (hip error {dq4_last_hip_error()})")
+    raise ValueError(msg)
+
+
+# ----------------------------------------------------------------------------
+# torch-tensor forms (allocating, or writing into `out`)
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _out_code(dtype) -> int:
+    torch = _torch()
+    codes = {torch.float32: DQ4_F32, torch.float16: DQ4_F16, torch.bfloat16: DQ4_BF16}
+    if dtype not in codes:
+        raise ValueError(f"unsupported output dtype {dtype}")
+    return codes[dtype]
+
+
+def _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                  end: int, blocksize: int, nested_blocksize: int):
+    torch = _torch()
+    tensors = (packed, scale_codes, nested_absmax, scale_codebook, codebook4)
+    device = packed.device
+    if device.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
+    for name, t, dt in zip(("packed", "scale_codes", "nested_absmax", "scale_codebook",
+                            "codebook4"), tensors,
+                           (torch.uint8, torch.uint8, torch.float32, torch.float32,
+                            torch.float32)):
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale_codebook.numel() != 256:
+        raise ValueError("scale_codebook must hold 256 values")
+    if codebook4.numel() != 16:
+        raise ValueError("codebook4 must hold 16 values")
+    if end > 0 and blocksize > 0 and nested_blocksize > 0:
+        nb = -(-end // blocksize)
+        ng = -(-nb // nested_blocksize)
+        if packed.numel() < -(-end // 2):
+            raise ValueError(f"packed holds {packed.numel()} bytes, needs {-(-end // 2)}")
+        if scale_codes.numel() < nb:
+            raise ValueError(f"scale_codes holds {scale_codes.numel()} codes, needs {nb}")
+        if nested_absmax.numel() < ng:
+            raise ValueError(f"nested_absmax holds {nested_absmax.numel()} values, needs {ng}")
+    return device
+
+
+def _prepare_out(out, count: int, dtype, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty(count, dtype=dtype, device=device)
+    if out.device != device or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the output dtype on the inputs' device")
+    if out.numel() < count:
+        raise ValueError(f"out holds {out.numel()} elements, needs {count}")
+    return out
+
+
+def _stream_handle(device, stream) -> ctypes.c_void_p:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dq4_nested_dequant(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                       offset: float, n: int, blocksize: int,
+                       nested_blocksize: int = NESTED_BLOCKSIZE, out_dtype=None,
+                       out=None, stream=None):
+    """Dequantize the first n elements; returns `out` (allocated when None).
+
+    Enqueued on `stream` (default: torch's current stream on the inputs'
+    device); asynchronous like any kernel launch.
+    """
+    torch = _torch()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    code = _out_code(out_dtype)
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           int(n), int(blocksize), int(nested_blocksize))
+    out = _prepare_out(out, max(int(n), 0), out_dtype, device)
+    with torch.cuda.device(device):
+        st = library().dq4_nested_dequant(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), int(n),
+            int(blocksize), int(nested_blocksize), code, out.data_ptr(),
+            _stream_handle(device, stream))
+    _raise_for(st, "dq4_nested_dequant")
+    return out
+
+
+def dq4_nested_dequant_rows(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                            offset: float, n_rows: int, n_cols: int, r0: int, rows: int,
+                            blocksize: int, nested_blocksize: int = NESTED_BLOCKSIZE,
+                            out_dtype=None, out=None, stream=None):
+    """Dequantize rows [r0, r0+rows) of an n_rows x n_cols weight into rows*n_cols elements."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    code = _out_code(out_dtype)
+    n_rows, n_cols, r0, rows = int(n_rows), int(n_cols), int(r0), int(rows)
+    if n_rows < 0 or n_cols < 0 or r0 < 0 or rows < 0 or r0 + rows > n_rows:
+        raise ValueError(f"row window [{r0}, {r0 + rows}) outside 0..{n_rows}")
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           (r0 + rows) * n_cols, int(blocksize), int(nested_blocksize))
+    out = _prepare_out(out, rows * n_cols, out_dtype, device)
+    with torch.cuda.device(device):
+        st = library().dq4_nested_dequant_rows(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), n_rows,
+            n_cols, r0, rows, int(blocksize), int(nested_blocksize), code, out.data_ptr(),
+            _stream_handle(device, stream))
+    _raise_for(st, "dq4_nested_dequant_rows")
+    return out
+
+
+def to_device(x, device="cuda"):
+    """Upload host inputs (block_wise_bit_amd.inputs.NestedInputs) as GPU tensors."""
+    torch = _torch()
+    return dict(
+        packed=torch.from_numpy(x.packed).to(device),
+        scale_codes=torch.from_numpy(x.scale_codes).to(device),
+        nested_absmax=torch.from_numpy(x.nested_absmax).to(device),
+        scale_codebook=torch.from_numpy(x.scale_codebook).to(device),
+        codebook4=torch.from_numpy(x.codebook4).to(device),
+    )

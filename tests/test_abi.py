@@ -1,0 +1,122 @@
+"""C ABI of libdq4.so, checked without a GPU.
+
+The library must load, export every function include/dq4.h declares, and
+reject bad arguments on the host before anything is enqueued (these calls
+return before any HIP runtime call, so they run on a machine without a GPU).
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import block_wise_bit_amd as dq4
+from libs import ensure_hip_library
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_hip_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = dq4.header_functions()
+    assert set(names) == {"dq4_nested_dequant", "dq4_nested_dequant_rows", "dq4_rows_per_block",
+                          "dq4_status_string", "dq4_last_hip_error"}
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding keeps the C names
+    for name in names:
+        assert callable(getattr(dq4, name)), name
+
+
+def test_status_strings(lib):
+    for st in (dq4.DQ4_OK, dq4.DQ4_EINVAL, dq4.DQ4_EUNSUPPORTED, dq4.DQ4_EHIP, 99):
+        s = dq4.dq4_status_string(st)
+        assert s.startswith("DQ4")
+    assert dq4.dq4_last_hip_error() == 0
+
+
+def _call(lib, n=64, blocksize=64, nested=256, dtype=dq4.DQ4_F16, ptr=1, out=1):
+    # fake non-null device pointers: every call here must fail validation or be a no-op
+    p = ctypes.c_void_p(ptr) if ptr else None
+    o = ctypes.c_void_p(out) if out else None
+    return lib.dq4_nested_dequant(p, p, p, p, p, ctypes.c_float(0.03), n, blocksize, nested, dtype,
+                                  o, None)
+
+
+def test_validation_whole_tensor(lib):
+    assert _call(lib, n=0) == dq4.DQ4_OK                          # no-op
+    assert _call(lib, n=0, ptr=0, out=0) == dq4.DQ4_OK            # no-op, null pointers allowed
+    assert _call(lib, n=-1) == dq4.DQ4_EINVAL
+    assert _call(lib, ptr=0) == dq4.DQ4_EINVAL
+    assert _call(lib, out=0) == dq4.DQ4_EINVAL
+    assert _call(lib, dtype=3) == dq4.DQ4_EINVAL
+    assert _call(lib, dtype=-1) == dq4.DQ4_EINVAL
+    for bs in (0, 16, 48, 100, 8192, -64):
+        assert _call(lib, blocksize=bs) == dq4.DQ4_EUNSUPPORTED, bs
+    for nested in (0, 128, 512):
+        assert _call(lib, nested=nested) == dq4.DQ4_EUNSUPPORTED
+
+
+def _call_rows(lib, n_rows=10, n_cols=64, r0=0, rows=1, blocksize=64, dtype=dq4.DQ4_F32, ptr=1):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dq4_nested_dequant_rows(p, p, p, p, p, ctypes.c_float(0.0), n_rows, n_cols, r0,
+                                       rows, blocksize, 256, dtype, p, None)
+
+
+def test_validation_rows(lib):
+    assert _call_rows(lib, rows=0) == dq4.DQ4_OK
+    assert _call_rows(lib, r0=10, rows=0) == dq4.DQ4_OK
+    assert _call_rows(lib, n_cols=0, rows=3) == dq4.DQ4_OK
+    assert _call_rows(lib, r0=-1) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, rows=-1) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, r0=9, rows=2) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, r0=11, rows=0) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, n_rows=-1) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, n_rows=1 << 40, n_cols=1 << 40) == dq4.DQ4_EINVAL   # overflow
+    assert _call_rows(lib, ptr=0) == dq4.DQ4_EINVAL
+    assert _call_rows(lib, blocksize=24) == dq4.DQ4_EUNSUPPORTED
+    assert _call_rows(lib, dtype=7) == dq4.DQ4_EINVAL
+
+
+def test_rows_per_block_worked_examples(lib):
+    with open(os.path.join(GOLDEN, "rows_per_block.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            n_cols, elem, budget, n_rows, rpb, windows, last = (
+                None if v == "-" else int(v) for v in line.split())
+            got = dq4.dq4_rows_per_block(n_cols, elem, budget)
+            if rpb is not None:
+                assert got == rpb
+            w = dq4.dq4_row_windows(n_rows, n_cols, elem, budget)
+            assert len(w) == windows
+            assert sum(r for _, r in w) == n_rows
+            if last is not None:
+                assert w[-1][1] == last
+    assert dq4.dq4_rows_per_block(0, 4, 1 << 28) == 1
+    assert dq4.dq4_rows_per_block(256, 4, 0) == 1
+
+
+def test_binding_rejects_host_tensors(lib):
+    torch = pytest.importorskip("torch")
+    u8 = torch.zeros(64, dtype=torch.uint8)
+    f = torch.zeros(256, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        dq4.dq4_nested_dequant(u8, u8, f, f, f[:16], 0.0, 64, 64)
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package and its build never import, load or name the oracle."""
+    pkg = os.path.dirname(dq4.__file__)
+    for root, _, files in os.walk(pkg):
+        for fname in files:
+            if fname.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(root, fname)) as fh:
+                    text = fh.read()
+                assert "import oracle" not in text and "from oracle" not in text, fname
+                assert "dq4o_" not in text and "dq4_oracle" not in text, fname
