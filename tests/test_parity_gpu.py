@@ -310,8 +310,8 @@ def test_beyond_2_pow_31_elements():
     dev = dq4.to_device(x)
     y = dq4.dq4_nested_dequant(**dev, offset=float(x.offset), n=n, blocksize=B,
                                out_dtype=torch.float16)
-    for first, count in ((0, 1 << 20), ((1 << 31) - (1 << 19), 1 << 20), (n - 5000, 5000),
-                         (1 << 30, 4096)):
+    for first, count in ((0, 1 << 20), ((1 << 31) - (1 << 19), n - (1 << 31) + (1 << 19)),
+                         (n - 5000, 5000), (1 << 30, 4096)):
         got = bits_of(y[first: first + count])
         assert_bits_equal(got, oracle_bits(x, "f16", first, count), f"range {first}+{count}")
     del y, dev
