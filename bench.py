@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dequantized GB/s (fraction of HBM peak), NF4→FP16 28672×8192 bs64"
 HBM_PEAK_GBS = 8000.0
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "dq4_vec_kernel_f16_28672x8192_bs64_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "dq4_tile_kernel_f16_28672x8192_bs64_pmc.json")
 KERNEL_SOURCE = os.path.join(ROOT, "block_wise_bit_amd", "csrc", "dq4.hip")
 
 

@@ -11,22 +11,28 @@
 // -ffp-contract=off on the command line), and the build is checked for the
 // absence of fused multiply-add instructions in the emitted gfx950 code.
 //
-// Design (HBM-bound stream; no matrix cores: nothing here is a contraction):
-//  * one workgroup of 256 lanes handles tiles of 256 * U packed dwords; lane
-//    t takes dword u * 256 + t of the tile, so every load instruction of a
-//    wavefront reads 256 contiguous bytes and every store instruction writes
-//    64 contiguous 16-byte (FP16/BF16) or 32-byte (FP32) pieces;
-//  * a dword holds 8 elements, and since blocksize >= 32 and the window
-//    starts on a multiple of 8, the 8 elements share one outer block: one
-//    code byte, one absmax and one rebuilt scale per lane and dword;
+// Design (an HBM-bound stream, 0.5 B read per 2 or 4 B written; no matrix
+// cores: nothing here is a contraction):
+//  * one workgroup of 256 lanes per tile of 8192 elements (4 KiB packed in,
+//    16 or 32 KiB out).  Lane t takes packed dword u * 256 + t of the tile
+//    (u = 0..3), so each wavefront load reads 256 contiguous bytes and each
+//    store instruction writes 1 KiB contiguous.  One tile per workgroup, in
+//    dispatch order, keeps the set of addresses being written compact; on
+//    MI355X this writes markedly faster than a persistent grid-stride loop;
+//  * the packed loads are issued first; while they are in flight the
+//    workgroup rebuilds the scale of each outer block its tile touches (at
+//    most 257), one block per lane, into LDS -- so the scale is computed once
+//    per block, never stored to HBM, and the value pass reads it from LDS;
 //  * the 256-entry scale codebook and the 16-entry value codebook sit in LDS;
-//    a 16-entry table covers 16 distinct banks, so lookups never conflict;
-//  * the grid is a few workgroups per compute unit, striding over the tiles
-//    so that the LDS tables are filled once per workgroup;
-//  * a tile that is not full, and any window that does not meet the
-//    alignment of the vector path, goes through a per-element path that
-//    computes the same bits.
-// No scratch memory: the scale never leaves registers.
+//    the 16-entry table covers 16 distinct banks, so lookups never conflict;
+//  * a dword holds 8 elements; since blocksize >= 32 and the window starts on
+//    a multiple of 8, the 8 elements share one outer block;
+//  * outputs are written with non-temporal stores (streamed, not kept in
+//    cache);
+//  * the partial last tile, and any window that does not meet the alignment
+//    of the vector path, go through a per-element path that computes the same
+//    bits.
+// No scratch memory: nothing but the inputs and the output touches HBM.
 
 #include <hip/hip_runtime.h>
 
@@ -41,10 +47,12 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNestedLog2 = 8;            // 256 outer blocks per nested absmax
-constexpr int kTileDwordsPerLane = 4;     // U
-constexpr int kTileElems = kThreads * kTileDwordsPerLane * 8;
-constexpr int kBlocksPerCU = 8;
+constexpr int kNestedLog2 = 8;                 // 256 outer blocks per nested absmax
+constexpr int kDwordsPerLane = 4;
+constexpr int kTileDwords = kThreads * kDwordsPerLane;
+constexpr int kTileElems = kTileDwords * 8;    // 8192
+constexpr int kMaxTileBlocks = kTileElems / 32 + 1;  // blocksize 32, tile not block-aligned
+constexpr int kElemBlocksPerCU = 8;            // grid of the per-element path
 
 struct Args {
     const uint8_t *packed;
@@ -59,12 +67,15 @@ struct Args {
     int log2_block;
 };
 
-// Scale of outer block b: a rounded multiply, then a rounded add.
-__device__ __forceinline__ float block_scale(const float *lds_scb, const Args &a,
-                                             uint32_t code, float absmax)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Scale of one outer block: a rounded multiply, then a rounded add.
+__device__ __forceinline__ float block_scale(float scale_codebook_value, float absmax,
+                                             float offset)
 {
-    const float t = lds_scb[code] * absmax;
-    return t + a.offset;
+    const float t = scale_codebook_value * absmax;
+    return t + offset;
 }
 
 // The FP32 product must be rounded to FP32 before it is converted: without
@@ -90,28 +101,43 @@ __device__ __forceinline__ __bf16 to_bf16(float x)
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 {
-    const _Float16 l = to_f16(lo);
-    const _Float16 h = to_f16(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_f16(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_f16(hi))) << 16);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    const __bf16 l = to_bf16(lo);
-    const __bf16 h = to_bf16(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_bf16(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_bf16(hi))) << 16);
 }
 
-// One element, any alignment: used for partial tiles and unaligned windows.
+__device__ __forceinline__ void stream_store(u32x4 *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
+// Fill the two codebooks in LDS (every lane must call it; ends on a barrier).
+__device__ __forceinline__ void load_tables(const Args &a, float *lds_scb, float *lds_cb4)
+{
+    const int t = threadIdx.x;
+    const float sv = a.scale_codebook[t];
+    const float cv = t < 16 ? a.codebook4[t] : 0.0f;
+    lds_scb[t] = sv;
+    if (t < 16)
+        lds_cb4[t] = cv;
+    __syncthreads();
+}
+
+// One element, any alignment: used for the partial last tile and for windows
+// the vector path cannot take.  j is the index within the window.
 template <int OUT>
 __device__ __forceinline__ void one_element(const Args &a, const float *lds_scb,
                                             const float *lds_cb4, int64_t j)
 {
     const int64_t i = a.e0 + j;
     const int64_t b = i >> a.log2_block;
-    const float s = block_scale(lds_scb, a, a.scale_codes[b], a.nested_absmax[b >> kNestedLog2]);
+    const float s = block_scale(lds_scb[a.scale_codes[b]], a.nested_absmax[b >> kNestedLog2],
+                                a.offset);
     const uint32_t byte = a.packed[i >> 1];
     const uint32_t k = (i & 1) ? (byte >> 4) : (byte & 0xFu);
     const float v = lds_cb4[k] * s;
@@ -124,73 +150,89 @@ __device__ __forceinline__ void one_element(const Args &a, const float *lds_scb,
     }
 }
 
-__device__ __forceinline__ void load_tables(const Args &a, float *lds_scb, float *lds_cb4)
-{
-    const int t = threadIdx.x;
-    lds_scb[t] = a.scale_codebook[t];
-    if (t < 16)
-        lds_cb4[t] = a.codebook4[t];
-    __syncthreads();
-}
-
-// Vector path.  Requires: e0 % 8 == 0, packed + e0/2 4-byte aligned, out
+// Vector path.  Requires e0 % 8 == 0, packed + e0/2 4-byte aligned and out
 // 16-byte aligned.  Tiles [0, n_full) are full; tile n_full (if any) is the
-// partial last tile.
+// partial last tile.  Normally gridDim.x == n_tiles and each workgroup runs
+// one tile; the loop only matters for grids capped below the tile count.
 template <int OUT>
-__global__ __launch_bounds__(kThreads) void dq4_vec_kernel(Args a, int64_t n_full,
-                                                           int64_t n_tiles)
+__global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_full,
+                                                            int64_t n_tiles)
 {
     __shared__ float lds_scb[256];
     __shared__ float lds_cb4[16];
-    load_tables(a, lds_scb, lds_cb4);
+    __shared__ float lds_scale[kMaxTileBlocks];
 
     const int t = threadIdx.x;
     const uint32_t *words = reinterpret_cast<const uint32_t *>(a.packed + (a.e0 >> 1));
-    constexpr int U = kTileDwordsPerLane;
+    const int lb = a.log2_block;
 
     for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        const int64_t tile_dword0 = tile * (kThreads * U);
+        const int64_t d0 = tile * kTileDwords;  // first packed dword of the tile
         if (tile >= n_full) {
-            // partial last tile: element by element
-            const int64_t first = tile_dword0 * 8;
-            for (int64_t j = first + t; j < a.count; j += kThreads)
+            load_tables(a, lds_scb, lds_cb4);
+            for (int64_t j = d0 * 8 + t; j < a.count; j += kThreads)
                 one_element<OUT>(a, lds_scb, lds_cb4, j);
+            __syncthreads();
             continue;
         }
 
-        uint32_t w[U];
-        uint32_t code[U];
-        float absmax[U];
+        // 1. packed data first: the longest-latency loads
+        uint32_t w[kDwordsPerLane];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t d = tile_dword0 + u * kThreads + t;
-            w[u] = words[d];
-            const int64_t b = (a.e0 + d * 8) >> a.log2_block;
-            code[u] = a.scale_codes[b];
-            absmax[u] = a.nested_absmax[b >> kNestedLog2];
+        for (int u = 0; u < kDwordsPerLane; ++u)
+            w[u] = words[d0 + u * kThreads + t];
+
+        // 2. metadata of the outer blocks this tile touches, one block per lane
+        const int64_t e_tile = a.e0 + d0 * 8;
+        const int64_t b0 = e_tile >> lb;
+        const uint32_t r = static_cast<uint32_t>(e_tile - (b0 << lb));  // offset in block b0
+        const int n_blocks = static_cast<int>((r + kTileElems - 1) >> lb) + 1;
+        const bool has0 = t < n_blocks;
+        const bool has1 = t + kThreads < n_blocks;
+        uint32_t code0 = 0, code1 = 0;
+        float absmax0 = 0.0f, absmax1 = 0.0f;
+        if (has0) {
+            code0 = a.scale_codes[b0 + t];
+            absmax0 = a.nested_absmax[(b0 + t) >> kNestedLog2];
         }
+        if (has1) {
+            code1 = a.scale_codes[b0 + t + kThreads];
+            absmax1 = a.nested_absmax[(b0 + t + kThreads) >> kNestedLog2];
+        }
+
+        // 3. codebooks to LDS, then every block's scale to LDS
+        load_tables(a, lds_scb, lds_cb4);
+        if (has0)
+            lds_scale[t] = block_scale(lds_scb[code0], absmax0, a.offset);
+        if (has1)
+            lds_scale[t + kThreads] = block_scale(lds_scb[code1], absmax1, a.offset);
+        __syncthreads();
+
+        // 4. value pass: 8 elements per dword, one 16-byte (or two) store(s)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t d = tile_dword0 + u * kThreads + t;
-            const float s = block_scale(lds_scb, a, code[u], absmax[u]);
+        for (int u = 0; u < kDwordsPerLane; ++u) {
+            const uint32_t dl = u * kThreads + t;
+            const float s = lds_scale[(r + dl * 8) >> lb];
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 v[e] = lds_cb4[(w[u] >> (4 * e)) & 0xFu] * s;
+            const int64_t d = d0 + dl;
             if constexpr (OUT == DQ4_F32) {
-                float4 *o = reinterpret_cast<float4 *>(a.out) + d * 2;
-                o[0] = make_float4(v[0], v[1], v[2], v[3]);
-                o[1] = make_float4(v[4], v[5], v[6], v[7]);
+                f32x4 *o = reinterpret_cast<f32x4 *>(a.out) + d * 2;
+                __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, o);
+                __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, o + 1);
             } else if constexpr (OUT == DQ4_F16) {
-                uint4 *o = reinterpret_cast<uint4 *>(a.out) + d;
-                *o = make_uint4(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
-                                pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7]));
+                stream_store(reinterpret_cast<u32x4 *>(a.out) + d,
+                             u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
+                                   pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])});
             } else {
-                uint4 *o = reinterpret_cast<uint4 *>(a.out) + d;
-                *o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+                stream_store(reinterpret_cast<u32x4 *>(a.out) + d,
+                             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
             }
         }
+        __syncthreads();  // LDS is rewritten by the next tile of this workgroup
     }
 }
 
@@ -211,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void dq4_elem_kernel(Args a)
 // host side
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 std::atomic<int> g_cu_count[kMaxDevices];
 thread_local int32_t t_last_hip_error = 0;
 
@@ -262,24 +305,24 @@ dq4_status_t hip_failed(hipError_t e)
 template <int OUT>
 dq4_status_t launch_typed(const Args &a, hipStream_t stream)
 {
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess)
-        return hip_failed(e);
-    const int64_t max_grid = static_cast<int64_t>(compute_units(device)) * kBlocksPerCU;
-
+    Args args = a;
+    hipError_t e;
     const bool vec = (a.e0 % 8 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.packed + (a.e0 >> 1)) % 4 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.out) % 16 == 0);
-    Args args = a;
     if (vec) {
-        const int64_t n_full = a.count / kTileElems;
-        const int64_t n_tiles = (a.count + kTileElems - 1) / kTileElems;
-        const int64_t grid = n_tiles < max_grid ? n_tiles : max_grid;
-        void *params[] = {&args, const_cast<int64_t *>(&n_full), const_cast<int64_t *>(&n_tiles)};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4_vec_kernel<OUT>),
+        int64_t n_full = a.count / kTileElems;
+        int64_t n_tiles = (a.count + kTileElems - 1) / kTileElems;
+        const int64_t grid = n_tiles < kMaxGrid ? n_tiles : kMaxGrid;
+        void *params[] = {&args, &n_full, &n_tiles};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4_tile_kernel<OUT>),
                             dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, stream);
     } else {
+        int device = 0;
+        e = hipGetDevice(&device);
+        if (e != hipSuccess)
+            return hip_failed(e);
+        const int64_t max_grid = static_cast<int64_t>(compute_units(device)) * kElemBlocksPerCU;
         const int64_t want = (a.count + kThreads - 1) / kThreads;
         const int64_t grid = want < max_grid ? want : max_grid;
         void *params[] = {&args};

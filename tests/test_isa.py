@@ -42,7 +42,7 @@ def _kernel_bodies(asm):
 
 def test_kernels_present(asm):
     names = list(_kernel_bodies(asm))
-    assert sum("dq4_vec_kernel" in n for n in names) == 3
+    assert sum("dq4_tile_kernel" in n for n in names) == 3
     assert sum("dq4_elem_kernel" in n for n in names) == 3
 
 
