@@ -21,7 +21,6 @@ reported with median, p10 and p90.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -34,7 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "dequantized GB/s (fraction of HBM peak), NF4→FP16 28672×8192 bs64"
 HBM_PEAK_GBS = 8000.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "dq4_tile_kernel_f16_28672x8192_bs64_pmc.json")
-KERNEL_SOURCE = os.path.join(ROOT, "block_wise_bit_amd", "csrc", "dq4.hip")
+KERNEL_DIGESTS = os.path.join(ROOT, "block_wise_bit_amd", "libdq4_kernels.json")
+HEADLINE_KERNEL = "_ZN3dq412_GLOBAL__N_115dq4_tile_kernelILi1EEEvNS0_4ArgsEll"
 
 
 def algorithmic_bytes(n: int, blocksize: int, out_bytes: int, nested: int = 256) -> int:
@@ -44,20 +44,25 @@ def algorithmic_bytes(n: int, blocksize: int, out_bytes: int, nested: int = 256)
     return (n + 1) // 2 + nb + 4 * ng + 4 * (256 + 16) + out_bytes * n
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def kernel_digest(symbol: str = HEADLINE_KERNEL):
+    """Instruction digest of the built kernel (written by the library build)."""
+    try:
+        with open(KERNEL_DIGESTS) as fh:
+            return json.load(fh).get(symbol)
+    except (OSError, ValueError):
+        return None
 
 
 def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    """HBM bytes per launch from the committed counter summary, if the
+    counters were taken on exactly the kernel code built now; else None."""
     try:
         with open(PMC_SUMMARY) as fh:
             s = json.load(fh)
     except (OSError, ValueError):
         return None
-    if s.get("kernel_source_sha256_16") != kernel_source_digest():
+    digest = kernel_digest(s.get("kernel_symbol", HEADLINE_KERNEL))
+    if digest is None or s.get("kernel_isa_sha256_16") != digest:
         return None
     return s.get("hbm_bytes_per_launch")
 
@@ -93,6 +98,141 @@ def copy_calibration(args, torch) -> int:
     return 0
 
 
+PRIMARY_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (28672, 8192))
+
+
+def compare_unfused(args, torch, dq4, inputs) -> int:
+    """Fused single kernel vs the unfused three-launch sequence on the primary
+    standalone matrix of the bitsandbytes issue's evidence plan: NF4 and FP4,
+    FP16 and BF16 (FP32 as control), block size 64, five weight shapes.
+    Baseline and candidate are interleaved batch by batch; each cell cycles
+    enough buffer sets that no set is reused within ~1 GB of traffic."""
+    import math
+
+    cells = []
+    for rows, cols in PRIMARY_SHAPES:
+        n = rows * cols
+        for fmt in ("nf4", "fp4"):
+            x = inputs.make_inputs(n, 64, fmt, -0.02, seed=inputs.SEED_BASE + 2, n_rows=rows,
+                                   n_cols=cols)
+            for dt, tdt, ob in (("f16", torch.float16, 2), ("bf16", torch.bfloat16, 2),
+                                ("f32", torch.float32, 4)):
+                alg = algorithmic_bytes(n, 64, ob)
+                n_sets = max(2, math.ceil(1.2e9 / alg))
+                ws_len = dq4.dq4_unfused_workspace_bytes(n, 64) // 4
+                sets = [(dq4.to_device(x, "cuda:0"), torch.empty(n, dtype=tdt, device="cuda:0"),
+                         torch.empty(ws_len, dtype=torch.float32, device="cuda:0"))
+                        for _ in range(n_sets)]
+                stream = torch.cuda.current_stream()
+
+                # both launch on torch's current stream (the capture stream while a
+                # graph is being captured)
+                def fused(k):
+                    dev, out, _ = sets[k % n_sets]
+                    dq4.dq4_nested_dequant(**dev, offset=float(x.offset), n=n, blocksize=64,
+                                           out_dtype=tdt, out=out)
+
+                def unfused(k):
+                    dev, out, ws = sets[k % n_sets]
+                    dq4.dq4_nested_dequant_unfused(**dev, offset=float(x.offset), n=n,
+                                                   blocksize=64, out_dtype=tdt, out=out,
+                                                   scale_workspace=ws)
+
+                for k in range(args.warmup):
+                    fused(k)
+                    unfused(k)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for k in range(5):
+                    fused(k)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                inner = max(5, int(2000.0 / max(e0.elapsed_time(e1) * 1e3 / 5, 1.0)))
+
+                # device time: `inner` calls captured in one HIP graph and replayed,
+                # so host-side launch cost is out and only the GPU's work and its
+                # inter-kernel gaps remain
+                graphs = {}
+                for name, fn in (("fused", fused), ("unfused", unfused)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for k in range(inner):
+                            fn(k)
+                    g.replay()
+                    graphs[name] = g
+                torch.cuda.synchronize()
+
+                def timed(run):
+                    a, b = (torch.cuda.Event(enable_timing=True),
+                            torch.cuda.Event(enable_timing=True))
+                    a.record(torch.cuda.current_stream())
+                    run()
+                    b.record(torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    return a.elapsed_time(b) * 1e3 / inner
+
+                samples = {"fused": [], "unfused": [], "fused_eager": [], "unfused_eager": []}
+                for _ in range(max(7, args.batches)):   # baseline and candidate interleaved
+                    for name in ("fused", "unfused"):
+                        samples[name].append(timed(graphs[name].replay))
+                    for name, fn in (("fused_eager", fused), ("unfused_eager", unfused)):
+                        samples[name].append(timed(lambda: [fn(k) for k in range(inner)]))
+                del graphs
+                # the two paths must agree bit for bit on this cell
+                dev0, out0, ws0 = sets[0]
+                ref = dq4.dq4_nested_dequant(**dev0, offset=float(x.offset), n=n, blocksize=64,
+                                             out_dtype=tdt)
+                dq4.dq4_nested_dequant_unfused(**dev0, offset=float(x.offset), n=n, blocksize=64,
+                                               out_dtype=tdt, out=out0, scale_workspace=ws0)
+                iview = torch.int32 if ob == 4 else torch.int16
+                bit_equal = bool(torch.equal(ref.view(iview), out0.view(iview)))
+                del ref
+                med = {k: percentile(v, 0.5) for k, v in samples.items()}
+                f_med, u_med = med["fused"], med["unfused"]
+                cell = {"shape": f"{rows}x{cols}", "format": fmt, "out": dt,
+                        "fused_us": round(f_med, 2), "unfused_us": round(u_med, 2),
+                        "speedup": round(u_med / f_med, 4),
+                        "fused_p10_p90": [round(percentile(samples["fused"], q), 2)
+                                          for q in (0.1, 0.9)],
+                        "unfused_p10_p90": [round(percentile(samples["unfused"], q), 2)
+                                            for q in (0.1, 0.9)],
+                        "fused_GBps": round(alg / (f_med * 1e-6) / 1e9, 1),
+                        "eager_fused_us": round(med["fused_eager"], 2),
+                        "eager_unfused_us": round(med["unfused_eager"], 2),
+                        "eager_speedup": round(med["unfused_eager"] / med["fused_eager"], 4),
+                        "samples_us": {k: [round(x, 2) for x in v] for k, v in samples.items()},
+                        "buffer_sets": n_sets, "inner": inner, "bit_equal": bit_equal}
+                cells.append(cell)
+                print(f"[compare] {cell['shape']} {fmt} {dt}: fused {f_med:.2f} us, "
+                      f"unfused {u_med:.2f} us, x{u_med / f_med:.3f} (eager "
+                      f"{cell['eager_fused_us']:.2f} / {cell['eager_unfused_us']:.2f} us)",
+                      file=sys.stderr, flush=True)
+                del sets
+                torch.cuda.empty_cache()
+
+    def geomean(vals):
+        return math.exp(sum(math.log(v) for v in vals) / len(vals))
+
+    primary = [c["speedup"] for c in cells if c["out"] in ("f16", "bf16")]
+    controls = [c["speedup"] for c in cells if c["out"] == "f32"]
+    eager = [c["eager_speedup"] for c in cells if c["out"] in ("f16", "bf16")]
+    all_equal = all(c["bit_equal"] for c in cells)
+    print(json.dumps({
+        "metric": "fused vs unfused nested dequant speedup, geomean over NF4/FP4 x FP16/BF16, "
+                  "bs64, primary standalone matrix",
+        "value": round(geomean(primary), 4), "unit": "x", "higher_is_better": True,
+        "fp32_control_geomean": round(geomean(controls), 4),
+        "eager_geomean": round(geomean(eager), 4),
+        "timing": "device time per call from HIP-graph replays of `inner` calls, median of "
+                  ">= 7 interleaved batches; eager_* = the same calls launched from Python",
+        "min_primary_speedup": round(min(primary), 4),
+        "fused_equals_unfused_bitwise": all_equal,
+        "n_gpus": 1, "warmup": args.warmup, "data": "synthetic", "cells": cells,
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+    return 0 if all_equal else 3
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +243,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (whole-tensor passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="instead of the benchmark, time the fused kernel against the unfused "
+                         "three-launch sequence over the primary standalone matrix")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of MIB "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -126,6 +269,8 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(args, torch)
     dq4.library()  # fail loudly if the HIP library is missing
+    if args.compare_unfused:
+        return compare_unfused(args, torch, dq4, inputs)
 
     wl = inputs.HEADLINE
     n, bs = wl.n, wl.blocksize
@@ -206,7 +351,7 @@ def main() -> int:
                       "median": round(percentile(batch_us, 0.5), 3),
                       "p10": round(percentile(batch_us, 0.1), 3),
                       "p90": round(percentile(batch_us, 0.9), 3)},
-        "kernel_source_sha256_16": kernel_source_digest(),
+        "kernel_isa_sha256_16": kernel_digest(),
         "device": torch.cuda.get_device_name(0),
         "cpu_baseline": None,
         "parity": None,

@@ -12,6 +12,8 @@ cannot be loaded, every call raises.
     dq4_nested_dequant_rows(..., n_rows, n_cols, r0, rows, ...) -> tensor
     dq4_rows_per_block(n_cols, elem_bytes, budget_bytes) -> int
     dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
+    dq4_nested_dequant_unfused(...) -> tensor     (three-launch comparison baseline)
+    dq4_unfused_workspace_bytes(n, blocksize) -> int
 """
 from __future__ import annotations
 
@@ -55,6 +57,10 @@ def library() -> ctypes.CDLL:
     lib.dq4_nested_dequant_rows.restype = i32
     lib.dq4_rows_per_block.argtypes = [i64, i64, i64]
     lib.dq4_rows_per_block.restype = i64
+    lib.dq4_nested_dequant_unfused.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32, P, P, P]
+    lib.dq4_nested_dequant_unfused.restype = i32
+    lib.dq4_unfused_workspace_bytes.argtypes = [i64, i32]
+    lib.dq4_unfused_workspace_bytes.restype = i64
     lib.dq4_status_string.argtypes = [i32]
     lib.dq4_status_string.restype = ctypes.c_char_p
     lib.dq4_last_hip_error.argtypes = []
@@ -85,6 +91,10 @@ def dq4_last_hip_error() -> int:
 def dq4_rows_per_block(n_cols: int, elem_bytes: int = 4,
                        budget_bytes: int = ROW_BLOCK_BUDGET_BYTES) -> int:
     return int(library().dq4_rows_per_block(int(n_cols), int(elem_bytes), int(budget_bytes)))
+
+
+def dq4_unfused_workspace_bytes(n: int, blocksize: int) -> int:
+    return int(library().dq4_unfused_workspace_bytes(int(n), int(blocksize)))
 
 
 def dq4_row_windows(n_rows: int, n_cols: int, elem_bytes: int = 4,
@@ -215,6 +225,36 @@ def dq4_nested_dequant_rows(packed, scale_codes, nested_absmax, scale_codebook, 
             n_cols, r0, rows, int(blocksize), int(nested_blocksize), code, out.data_ptr(),
             _stream_handle(device, stream))
     _raise_for(st, "dq4_nested_dequant_rows")
+    return out
+
+
+def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                               offset: float, n: int, blocksize: int,
+                               nested_blocksize: int = NESTED_BLOCKSIZE, out_dtype=None,
+                               out=None, scale_workspace=None, stream=None):
+    """The unfused three-launch sequence (comparison baseline); same results as
+    dq4_nested_dequant.  `scale_workspace` (FP32, >= ceil(n/blocksize)
+    values) is allocated when None."""
+    torch = _torch()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    code = _out_code(out_dtype)
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           int(n), int(blocksize), int(nested_blocksize))
+    out = _prepare_out(out, max(int(n), 0), out_dtype, device)
+    need = dq4_unfused_workspace_bytes(int(n), int(blocksize)) // 4
+    if scale_workspace is None:
+        scale_workspace = torch.empty(max(need, 1), dtype=torch.float32, device=device)
+    elif (scale_workspace.device != device or scale_workspace.dtype != torch.float32
+          or not scale_workspace.is_contiguous() or scale_workspace.numel() < need):
+        raise ValueError(f"scale_workspace must be a contiguous float32 tensor of >= {need} "
+                         "values on the inputs' device")
+    with torch.cuda.device(device):
+        st = library().dq4_nested_dequant_unfused(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), int(n),
+            int(blocksize), int(nested_blocksize), code, scale_workspace.data_ptr(),
+            out.data_ptr(), _stream_handle(device, stream))
+    _raise_for(st, "dq4_nested_dequant_unfused")
     return out
 
 

@@ -9,15 +9,20 @@ Flags that matter for the results:
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCE = os.path.join(PKG, "csrc", "dq4.hip")
+SOURCES = [os.path.join(PKG, "csrc", "dq4.hip"), os.path.join(PKG, "csrc", "dq4_unfused.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdq4.so")
+KERNEL_DIGESTS = os.path.join(PKG, "libdq4_kernels.json")  # written next to the library
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -40,20 +45,46 @@ def hipcc() -> str:
 def build(out: str = LIBRARY, extra_flags=()) -> str:
     """Compile the library; always recompiles.  Returns the .so path."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-shared", "-I", INCLUDE, "-o", tmp, SOURCE]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-shared", "-I", INCLUDE, "-o", tmp, *SOURCES]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    with tempfile.TemporaryDirectory() as d:
+        digests = kernel_digests(device_assembly(d))
+    with open(KERNEL_DIGESTS, "w") as fh:
+        json.dump(digests, fh, indent=1, sort_keys=True)
     return out
 
 
 def device_assembly(workdir: str) -> str:
     """gfx950 assembly of the library's kernels (for instruction checks)."""
     workdir = os.path.abspath(workdir)
-    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", "-I", INCLUDE,
-           "-o", os.path.join(workdir, "dq4-gfx950.s"), SOURCE]
-    subprocess.run(cmd, check=True, cwd=workdir)
-    with open(os.path.join(workdir, "dq4-gfx950.s")) as fh:
-        return fh.read()
+    parts = []
+    for src in SOURCES:
+        out = os.path.join(workdir, os.path.basename(src) + "-gfx950.s")
+        cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", "-I", INCLUDE, "-o", out, src]
+        subprocess.run(cmd, check=True, cwd=workdir)
+        with open(out) as fh:
+            parts.append(fh.read())
+    return "\n".join(parts)
+
+
+def kernel_bodies(asm: str) -> dict:
+    """{kernel symbol: its instructions, comments and directives dropped}."""
+    bodies = {}
+    for m in re.finditer(r"^(_Z\w+):.*?$(.*?)^\s*s_endpgm", asm, flags=re.M | re.S):
+        lines = []
+        for line in m.group(2).splitlines():
+            code = line.split(";")[0].strip()
+            if code and not code.startswith(".") and not code.endswith(":"):
+                lines.append(code)
+        bodies[m.group(1)] = "\n".join(lines)
+    return bodies
+
+
+def kernel_digests(asm: str) -> dict:
+    """{kernel symbol: sha256[:16] of its instructions}: identifies the exact
+    code a measurement was taken on, independent of source-level edits."""
+    return {k: hashlib.sha256(v.encode()).hexdigest()[:16] for k, v in kernel_bodies(asm).items()}
 
 
 if __name__ == "__main__":

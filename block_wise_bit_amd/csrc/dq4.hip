@@ -14,19 +14,21 @@
 // Design (an HBM-bound stream, 0.5 B read per 2 or 4 B written; no matrix
 // cores: nothing here is a contraction):
 //  * one workgroup of 256 lanes per tile of 8192 elements (4 KiB packed in,
-//    16 or 32 KiB out).  Lane t takes packed dword u * 256 + t of the tile
-//    (u = 0..3), so each wavefront load reads 256 contiguous bytes and each
-//    store instruction writes 1 KiB contiguous.  One tile per workgroup, in
-//    dispatch order, keeps the set of addresses being written compact; on
-//    MI355X this writes markedly faster than a persistent grid-stride loop;
+//    16 or 32 KiB out).  The tile is cut into "units" of 8 elements (one
+//    packed dword) for FP16/BF16 output or 4 elements (one packed 16-bit
+//    word) for FP32 output; lane t takes unit u * 256 + t, so each wavefront
+//    load is contiguous and each store instruction writes 64 x 16 contiguous
+//    bytes for every output type.  One tile per workgroup, in dispatch order,
+//    keeps the set of addresses being written compact; on MI355X this writes
+//    markedly faster than a persistent grid-stride loop;
 //  * the packed loads are issued first; while they are in flight the
 //    workgroup rebuilds the scale of each outer block its tile touches (at
 //    most 257), one block per lane, into LDS -- so the scale is computed once
 //    per block, never stored to HBM, and the value pass reads it from LDS;
 //  * the 256-entry scale codebook and the 16-entry value codebook sit in LDS;
 //    the 16-entry table covers 16 distinct banks, so lookups never conflict;
-//  * a dword holds 8 elements; since blocksize >= 32 and the window starts on
-//    a multiple of 8, the 8 elements share one outer block;
+//  * since blocksize >= 32 and the window starts on a multiple of 8, the
+//    elements of a unit share one outer block;
 //  * outputs are written with non-temporal stores (streamed, not kept in
 //    cache);
 //  * the partial last tile, and any window that does not meet the alignment
@@ -41,13 +43,14 @@
 #include <atomic>
 
 #include "dq4.h"
+#include "dq4_device.h"
 
 #pragma clang fp contract(off)
 
+namespace dq4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNestedLog2 = 8;                 // 256 outer blocks per nested absmax
 constexpr int kDwordsPerLane = 4;
 constexpr int kTileDwords = kThreads * kDwordsPerLane;
 constexpr int kTileElems = kTileDwords * 8;    // 8192
@@ -66,55 +69,6 @@ struct Args {
     float offset;
     int log2_block;
 };
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Scale of one outer block: a rounded multiply, then a rounded add.
-__device__ __forceinline__ float block_scale(float scale_codebook_value, float absmax,
-                                             float offset)
-{
-    const float t = scale_codebook_value * absmax;
-    return t + offset;
-}
-
-// The FP32 product must be rounded to FP32 before it is converted: without
-// this fence the compiler folds "multiply, then convert to FP16" into one
-// mixed-precision fused multiply-add (v_fma_mix*), which rounds the exact
-// product once, straight to FP16 -- a different result in about one element
-// in 20 000.  The empty asm makes the FP32 value opaque; it emits nothing.
-__device__ __forceinline__ float rounded_fp32(float x)
-{
-    __asm__("" : "+v"(x));
-    return x;
-}
-
-__device__ __forceinline__ _Float16 to_f16(float x)
-{
-    return static_cast<_Float16>(rounded_fp32(x));  // IEEE round to nearest even
-}
-
-__device__ __forceinline__ __bf16 to_bf16(float x)
-{
-    return static_cast<__bf16>(rounded_fp32(x));    // IEEE round to nearest even
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
-{
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_f16(lo))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_f16(hi))) << 16);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_bf16(lo))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, to_bf16(hi))) << 16);
-}
-
-__device__ __forceinline__ void stream_store(u32x4 *p, u32x4 v)
-{
-    __builtin_nontemporal_store(v, p);
-}
 
 // Fill the two codebooks in LDS (every lane must call it; ends on a barrier).
 __device__ __forceinline__ void load_tables(const Args &a, float *lds_scb, float *lds_cb4)
@@ -140,14 +94,7 @@ __device__ __forceinline__ void one_element(const Args &a, const float *lds_scb,
                                 a.offset);
     const uint32_t byte = a.packed[i >> 1];
     const uint32_t k = (i & 1) ? (byte >> 4) : (byte & 0xFu);
-    const float v = lds_cb4[k] * s;
-    if constexpr (OUT == DQ4_F32) {
-        static_cast<float *>(a.out)[j] = v;
-    } else if constexpr (OUT == DQ4_F16) {
-        static_cast<_Float16 *>(a.out)[j] = to_f16(v);
-    } else {
-        static_cast<__bf16 *>(a.out)[j] = to_bf16(v);
-    }
+    store1<OUT>(a.out, j, lds_cb4[k] * s);
 }
 
 // Vector path.  Requires e0 % 8 == 0, packed + e0/2 4-byte aligned and out
@@ -163,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
     __shared__ float lds_scale[kMaxTileBlocks];
 
     const int t = threadIdx.x;
-    const uint32_t *words = reinterpret_cast<const uint32_t *>(a.packed + (a.e0 >> 1));
     const int lb = a.log2_block;
 
     for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
@@ -177,10 +123,15 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         }
 
         // 1. packed data first: the longest-latency loads
-        uint32_t w[kDwordsPerLane];
+        using Word = typename Unit<OUT>::Word;
+        constexpr int E = Unit<OUT>::kElems;
+        constexpr int kUnits = 32 / E;  // units per lane and tile
+        const Word *words = reinterpret_cast<const Word *>(a.packed + (a.e0 >> 1));
+        const int64_t u0 = d0 * 8 / E;  // first unit of the tile
+        Word w[kUnits];
 #pragma unroll
-        for (int u = 0; u < kDwordsPerLane; ++u)
-            w[u] = words[d0 + u * kThreads + t];
+        for (int u = 0; u < kUnits; ++u)
+            w[u] = words[u0 + u * kThreads + t];
 
         // 2. metadata of the outer blocks this tile touches, one block per lane
         const int64_t e_tile = a.e0 + d0 * 8;
@@ -208,29 +159,16 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
             lds_scale[t + kThreads] = block_scale(lds_scb[code1], absmax1, a.offset);
         __syncthreads();
 
-        // 4. value pass: 8 elements per dword, one 16-byte (or two) store(s)
+        // 4. value pass: E elements per unit, one 16-byte store per unit
 #pragma unroll
-        for (int u = 0; u < kDwordsPerLane; ++u) {
-            const uint32_t dl = u * kThreads + t;
-            const float s = lds_scale[(r + dl * 8) >> lb];
-            float v[8];
+        for (int u = 0; u < kUnits; ++u) {
+            const uint32_t ul = u * kThreads + t;
+            const float s = lds_scale[(r + ul * E) >> lb];
+            float v[E];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = lds_cb4[(w[u] >> (4 * e)) & 0xFu] * s;
-            const int64_t d = d0 + dl;
-            if constexpr (OUT == DQ4_F32) {
-                f32x4 *o = reinterpret_cast<f32x4 *>(a.out) + d * 2;
-                __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, o);
-                __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, o + 1);
-            } else if constexpr (OUT == DQ4_F16) {
-                stream_store(reinterpret_cast<u32x4 *>(a.out) + d,
-                             u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
-                                   pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])});
-            } else {
-                stream_store(reinterpret_cast<u32x4 *>(a.out) + d,
-                             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
-            }
+            for (int e = 0; e < E; ++e)
+                v[e] = lds_cb4[(static_cast<uint32_t>(w[u]) >> (4 * e)) & 0xFu] * s;
+            store_unit<OUT>(a.out, u0 + ul, v);
         }
         __syncthreads();  // LDS is rewritten by the next tile of this workgroup
     }
@@ -249,13 +187,27 @@ __global__ __launch_bounds__(kThreads) void dq4_elem_kernel(Args a)
         one_element<OUT>(a, lds_scb, lds_cb4, j);
 }
 
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+namespace {
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 std::atomic<int> g_cu_count[kMaxDevices];
 thread_local int32_t t_last_hip_error = 0;
+
+int log2_if_pow2(int32_t x)
+{
+    if (x <= 0 || (x & (x - 1)) != 0)
+        return -1;
+    int r = 0;
+    while ((1 << r) != x)
+        ++r;
+    return r;
+}
+}  // namespace
 
 int compute_units(int device)
 {
@@ -271,17 +223,7 @@ int compute_units(int device)
     return cus;
 }
 
-int log2_if_pow2(int32_t x)
-{
-    if (x <= 0 || (x & (x - 1)) != 0)
-        return -1;
-    int r = 0;
-    while ((1 << r) != x)
-        ++r;
-    return r;
-}
-
-dq4_status_t validate_common(int32_t blocksize, int32_t nested_blocksize, int32_t out_dtype,
+dq4_status_t validate_layout(int32_t blocksize, int32_t nested_blocksize, int32_t out_dtype,
                              int *log2_block)
 {
     if (out_dtype != DQ4_F32 && out_dtype != DQ4_F16 && out_dtype != DQ4_BF16)
@@ -302,6 +244,12 @@ dq4_status_t hip_failed(hipError_t e)
     return DQ4_EHIP;
 }
 
+int32_t last_hip_error()
+{
+    return t_last_hip_error;
+}
+
+namespace {
 template <int OUT>
 dq4_status_t launch_typed(const Args &a, hipStream_t stream)
 {
@@ -352,8 +300,10 @@ bool any_null(const void *a, const void *b, const void *c, const void *d, const 
 {
     return !a || !b || !c || !d || !e || !f;
 }
-
 }  // namespace
+}  // namespace dq4
+
+using dq4::Args;
 
 extern "C" {
 
@@ -364,18 +314,18 @@ dq4_status_t dq4_nested_dequant(const uint8_t *packed, const uint8_t *scale_code
                                 void *out, void *stream)
 {
     int log2_block = 0;
-    const dq4_status_t st = validate_common(blocksize, nested_blocksize, out_dtype, &log2_block);
+    const dq4_status_t st = dq4::validate_layout(blocksize, nested_blocksize, out_dtype, &log2_block);
     if (st != DQ4_OK)
         return st;
     if (n < 0)
         return DQ4_EINVAL;
     if (n == 0)
         return DQ4_OK;
-    if (any_null(packed, scale_codes, nested_absmax, scale_codebook, codebook4, out))
+    if (dq4::any_null(packed, scale_codes, nested_absmax, scale_codebook, codebook4, out))
         return DQ4_EINVAL;
     const Args a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, out,
                  0, n, offset, log2_block};
-    return launch(a, out_dtype, stream);
+    return dq4::launch(a, out_dtype, stream);
 }
 
 dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale_codes,
@@ -386,7 +336,7 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
                                      void *stream)
 {
     int log2_block = 0;
-    const dq4_status_t st = validate_common(blocksize, nested_blocksize, out_dtype, &log2_block);
+    const dq4_status_t st = dq4::validate_layout(blocksize, nested_blocksize, out_dtype, &log2_block);
     if (st != DQ4_OK)
         return st;
     if (n_rows < 0 || n_cols < 0 || r0 < 0 || rows < 0 || r0 > n_rows || rows > n_rows - r0)
@@ -396,11 +346,11 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
     const int64_t count = rows * n_cols;
     if (count == 0)
         return DQ4_OK;
-    if (any_null(packed, scale_codes, nested_absmax, scale_codebook, codebook4, out))
+    if (dq4::any_null(packed, scale_codes, nested_absmax, scale_codebook, codebook4, out))
         return DQ4_EINVAL;
     const Args a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, out,
                  r0 * n_cols, count, offset, log2_block};
-    return launch(a, out_dtype, stream);
+    return dq4::launch(a, out_dtype, stream);
 }
 
 int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes)
@@ -431,7 +381,7 @@ const char *dq4_status_string(dq4_status_t status)
 
 int32_t dq4_last_hip_error(void)
 {
-    return t_last_hip_error;
+    return dq4::last_hip_error();
 }
 
 }  // extern "C"

@@ -37,10 +37,10 @@
  * Input and output ranges must not overlap.
  *
  * Ownership and ordering: the library allocates nothing, frees nothing, keeps
- * no handle to any buffer and never synchronizes.  Each call enqueues exactly
- * one kernel on `stream` (a hipStream_t; NULL means the legacy default
- * stream) and returns; the output is ready when that stream reaches the
- * kernel.  Calls are reentrant and thread-safe.
+ * no handle to any buffer and never synchronizes.  Each fused call enqueues
+ * exactly one kernel on `stream` (a hipStream_t; NULL means the legacy
+ * default stream) and returns; the output is ready when that stream reaches
+ * the kernel.  Calls are reentrant and thread-safe.
  *
  * Errors: validation happens on the host before anything is enqueued.  A call
  * that returns anything but DQ4_OK has enqueued nothing and left `out`
@@ -115,6 +115,32 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
  * Non-positive arguments return 1.  Host only.
  */
 int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes);
+
+/*
+ * Unfused three-launch form, kept as the comparison baseline of
+ * dq4_nested_dequant: the existing sequence of the bitsandbytes issue above
+ * (section "Problem") -- (1) scale codes to an FP32 scale buffer,
+ * scale[b] = fl32(scale_codebook[code[b]] * nested_absmax[b / 256]); (2) a
+ * separate elementwise add, scale[b] = fl32(scale[b] + offset); (3) the
+ * value pass reading that buffer.  Results are bitwise identical to
+ * dq4_nested_dequant; the cost is the FP32 buffer's HBM traffic and two more
+ * launches, which is what the fused call removes.
+ *
+ * scale_workspace: caller-owned device buffer of at least
+ *   dq4_unfused_workspace_bytes(n, blocksize) bytes; overwritten.  Three
+ *   kernels are enqueued on `stream`, in order.  Other arguments, errors and
+ *   the n == 0 no-op are as for dq4_nested_dequant.
+ */
+dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *scale_codes,
+                                        const float *nested_absmax,
+                                        const float *scale_codebook, const float *codebook4,
+                                        float offset, int64_t n, int32_t blocksize,
+                                        int32_t nested_blocksize, int32_t out_dtype,
+                                        float *scale_workspace, void *out, void *stream);
+
+/* Bytes of FP32 scale workspace dq4_nested_dequant_unfused needs: 4 * ceil(n /
+ * blocksize); 0 for non-positive arguments.  Host only. */
+int64_t dq4_unfused_workspace_bytes(int64_t n, int32_t blocksize);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *dq4_status_string(dq4_status_t status);

@@ -24,7 +24,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = dq4.header_functions()
     assert set(names) == {"dq4_nested_dequant", "dq4_nested_dequant_rows", "dq4_rows_per_block",
-                          "dq4_status_string", "dq4_last_hip_error"}
+                          "dq4_status_string", "dq4_last_hip_error",
+                          "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -59,6 +60,24 @@ def test_validation_whole_tensor(lib):
         assert _call(lib, blocksize=bs) == dq4.DQ4_EUNSUPPORTED, bs
     for nested in (0, 128, 512):
         assert _call(lib, nested=nested) == dq4.DQ4_EUNSUPPORTED
+
+
+def test_validation_unfused(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(n=64, blocksize=64, nested=256, dtype=dq4.DQ4_F16, ws=p):
+        return lib.dq4_nested_dequant_unfused(p, p, p, p, p, ctypes.c_float(0.0), n, blocksize,
+                                              nested, dtype, ws, p, None)
+    assert call(n=0) == dq4.DQ4_OK
+    assert call(n=-5) == dq4.DQ4_EINVAL
+    assert call(ws=None) == dq4.DQ4_EINVAL
+    assert call(blocksize=100) == dq4.DQ4_EUNSUPPORTED
+    assert call(nested=64) == dq4.DQ4_EUNSUPPORTED
+    assert call(dtype=9) == dq4.DQ4_EINVAL
+    assert dq4.dq4_unfused_workspace_bytes(1000, 64) == 4 * 16
+    assert dq4.dq4_unfused_workspace_bytes(1024, 64) == 4 * 16
+    assert dq4.dq4_unfused_workspace_bytes(1025, 64) == 4 * 17
+    assert dq4.dq4_unfused_workspace_bytes(0, 64) == 0
 
 
 def _call_rows(lib, n_rows=10, n_cols=64, r0=0, rows=1, blocksize=64, dtype=dq4.DQ4_F32, ptr=1):

@@ -34,24 +34,42 @@ def asm():
 
 
 def _kernel_bodies(asm):
-    bodies = {}
-    for m in re.finditer(r"^(_Z\w+):.*?$(.*?)^\s*s_endpgm", asm, flags=re.M | re.S):
-        bodies[m.group(1)] = m.group(2)
-    return bodies
+    return dq4_build.kernel_bodies(asm)
 
 
 def test_kernels_present(asm):
     names = list(_kernel_bodies(asm))
-    assert sum("dq4_tile_kernel" in n for n in names) == 3
-    assert sum("dq4_elem_kernel" in n for n in names) == 3
+    for kernel, count in (("dq4_tile_kernel", 3), ("dq4_elem_kernel", 3),
+                          ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
+                          ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1)):
+        assert sum(kernel in n for n in names) == count, kernel
 
 
 def test_no_fused_or_packed_fp_instructions(asm):
-    for name, body in _kernel_bodies(asm).items():
-        code = "\n".join(l.split(";")[0] for l in body.splitlines())
+    for name, code in _kernel_bodies(asm).items():
         found = sorted(set(FORBIDDEN.findall(code)))
         assert not found, f"{name}: {found}"
-        assert "v_mul_f32" in code and "v_add_f32" in code, name
+        if "add_offset" in name:
+            assert "v_add_f32" in code, name
+        else:
+            assert "v_mul_f32" in code, name
+        if "dq4_tile_kernel" in name or "dq4_elem_kernel" in name:
+            assert "v_add_f32" in code, name   # the scale is rebuilt in the fused kernels
+
+
+def test_kernel_digests_written_by_build():
+    """build() records the instruction digest of every kernel next to the
+    library, so a measurement can be tied to the exact code it ran."""
+    import json
+    import os
+    from libs import ensure_hip_library
+    ensure_hip_library()
+    if not os.path.exists(dq4_build.KERNEL_DIGESTS):
+        dq4_build.build()
+    with open(dq4_build.KERNEL_DIGESTS) as fh:
+        digests = json.load(fh)
+    assert any("dq4_tile_kernelILi1" in k for k in digests)
+    assert all(len(v) == 16 for v in digests.values())
 
 
 def test_ieee_float_modes(asm):
