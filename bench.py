@@ -233,6 +233,76 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
     return 0 if all_equal else 3
 
 
+def out_prod_bench(args, torch, dq4, inputs) -> int:
+    """Row-blocked out_prod of the 151936 x 5376 NF4 output head against a
+    src1 of m rows per weight row (the LoRA backward of the output head in
+    the llama.cpp PR): 13 F32 windows of <= 256 MiB, one FP32 GEMM each.
+    Reports the whole call, the dequantization share (the windows alone),
+    and the single-window whole-copy variant for comparison."""
+    wl = inputs.OUTPUT_HEAD
+    x = wl.inputs()
+    dev = dq4.to_device(x, "cuda:0")
+    m = args.out_prod_m
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    src1 = torch.randn((wl.n_rows, m), dtype=torch.float32, device="cuda:0", generator=g)
+    dst = torch.empty((m, wl.n_cols), dtype=torch.float32, device="cuda:0")
+    budget = 256 << 20
+    rows_pb = dq4.dq4_rows_per_block(wl.n_cols, 4, budget)
+    ws = torch.empty(rows_pb * wl.n_cols, dtype=torch.float32, device="cuda:0")
+    windows = dq4.dq4_row_windows(wl.n_rows, wl.n_cols, 4, budget)
+    flops = 2.0 * m * wl.n_rows * wl.n_cols
+
+    def timeit(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps  # ms
+
+    def blocked():
+        dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols,
+                              blocksize=64, src1=src1, dst=dst, workspace=ws)
+
+    def windows_only():
+        for r0, rows in windows:
+            dq4.dq4_nested_dequant_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows,
+                                        n_cols=wl.n_cols, r0=r0, rows=rows, blocksize=64,
+                                        out_dtype=torch.float32, out=ws)
+
+    reps = max(3, args.steps // 100)
+    t_blocked = timeit(blocked, reps)
+    t_dequant = timeit(windows_only, reps)
+    out_blocked = dst.clone()
+    whole = torch.empty(wl.n_rows * wl.n_cols, dtype=torch.float32, device="cuda:0")
+
+    def whole_copy():
+        dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols,
+                              blocksize=64, src1=src1, dst=dst, workspace=whole)
+
+    t_whole = timeit(whole_copy, reps)
+    rel = float((dst - out_blocked).abs().max() / out_blocked.abs().max().clamp_min(1e-30))
+    print(json.dumps({
+        "metric": "row-blocked out_prod of the 151936x5376 NF4 output head, FP32 GEMM TFLOP/s",
+        "value": round(flops / (t_blocked * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": wl.name, "m": m, "windows": len(windows),
+                   "rows_per_window": rows_pb, "transient_bytes": rows_pb * wl.n_cols * 4},
+        "ms_blocked": round(t_blocked, 4), "ms_dequant_windows": round(t_dequant, 4),
+        "dequant_share": round(t_dequant / t_blocked, 4),
+        "ms_whole_copy": round(t_whole, 4), "whole_copy_transient_bytes": whole.numel() * 4,
+        "blocked_vs_whole_max_rel_diff": rel,
+        "roofline": {"bound": "mfma", "achieved": round(flops / (t_blocked * 1e-3) / 1e12, 2),
+                     "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(flops / (t_blocked * 1e-3) / 1e12 / 157.3, 4)},
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +316,11 @@ def main() -> int:
     ap.add_argument("--compare-unfused", action="store_true",
                     help="instead of the benchmark, time the fused kernel against the unfused "
                          "three-launch sequence over the primary standalone matrix")
+    ap.add_argument("--out-prod", action="store_true",
+                    help="instead of the benchmark, time the row-blocked out_prod of the "
+                         "151936x5376 output head (FP32 GEMM per window)")
+    ap.add_argument("--out-prod-m", type=int, default=512,
+                    help="columns of src1 (tokens) for --out-prod")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of MIB "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -271,6 +346,8 @@ def main() -> int:
     dq4.library()  # fail loudly if the HIP library is missing
     if args.compare_unfused:
         return compare_unfused(args, torch, dq4, inputs)
+    if args.out_prod:
+        return out_prod_bench(args, torch, dq4, inputs)
 
     wl = inputs.HEADLINE
     n, bs = wl.n, wl.blocksize

@@ -14,6 +14,8 @@ cannot be loaded, every call raises.
     dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
     dq4_nested_dequant_unfused(...) -> tensor     (three-launch comparison baseline)
     dq4_unfused_workspace_bytes(n, blocksize) -> int
+    dq4_out_prod_rows(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
+                                                   (row-blocked out_prod, FP32 GEMM)
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(PKG_DIR, "libdq4.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "dq4.h")
 
-DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP = 0, 1, 2, 3
+DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP, DQ4_EBLAS = 0, 1, 2, 3, 4
 DQ4_F32, DQ4_F16, DQ4_BF16 = 0, 1, 2
 NESTED_BLOCKSIZE = 256
 ROW_BLOCK_BUDGET_BYTES = 256 << 20   # 256 MiB of F32 per transient row block
@@ -61,6 +63,11 @@ def library() -> ctypes.CDLL:
     lib.dq4_nested_dequant_unfused.restype = i32
     lib.dq4_unfused_workspace_bytes.argtypes = [i64, i32]
     lib.dq4_unfused_workspace_bytes.restype = i64
+    lib.dq4_out_prod_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, P, i64, i64, i32, P,
+                                      P, i64, P]
+    lib.dq4_out_prod_rows.restype = i32
+    lib.dq4_last_blas_status.argtypes = []
+    lib.dq4_last_blas_status.restype = i32
     lib.dq4_status_string.argtypes = [i32]
     lib.dq4_status_string.restype = ctypes.c_char_p
     lib.dq4_last_hip_error.argtypes = []
@@ -88,6 +95,10 @@ def dq4_last_hip_error() -> int:
     return int(library().dq4_last_hip_error())
 
 
+def dq4_last_blas_status() -> int:
+    return int(library().dq4_last_blas_status())
+
+
 def dq4_rows_per_block(n_cols: int, elem_bytes: int = 4,
                        budget_bytes: int = ROW_BLOCK_BUDGET_BYTES) -> int:
     return int(library().dq4_rows_per_block(int(n_cols), int(elem_bytes), int(budget_bytes)))
@@ -110,6 +121,8 @@ def _raise_for(status: int, what: str) -> None:
     msg = f"{what}: {dq4_status_string(status)}"
     if status == DQ4_EHIP:
         raise Dq4Error(f"{msg} (hip error {dq4_last_hip_error()})")
+    if status == DQ4_EBLAS:
+        raise Dq4Error(f"{msg} (rocblas status {dq4_last_blas_status()})")
     raise ValueError(msg)
 
 
@@ -256,6 +269,55 @@ def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codeboo
             out.data_ptr(), _stream_handle(device, stream))
     _raise_for(st, "dq4_nested_dequant_unfused")
     return out
+
+
+def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                      offset: float, n_rows: int, n_cols: int, blocksize: int, src1,
+                      src1_transposed: bool = False, dst=None, workspace=None,
+                      workspace_bytes: int = ROW_BLOCK_BUDGET_BYTES,
+                      nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
+    """dst[i][j] = sum_r B[r][i] * W[r][j] for the nested 4-bit weight W
+    (n_rows x n_cols), dequantized to FP32 in row windows of at most
+    `workspace_bytes` and accumulated by an FP32 GEMM per window.
+
+    src1 is FP32, 2-D with unit stride along its last dimension: shape
+    (n_rows, m) (B = src1) or, with src1_transposed, (m, n_rows) (B = src1^T).
+    Returns dst (m x n_cols, FP32).  `workspace` (FP32, at least one row of
+    n_cols) is allocated when None, sized min(workspace_bytes, whole weight).
+    """
+    torch = _torch()
+    n_rows, n_cols = int(n_rows), int(n_cols)
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           n_rows * n_cols, int(blocksize), int(nested_blocksize))
+    if src1.device != device or src1.dtype != torch.float32 or src1.dim() != 2:
+        raise ValueError("src1 must be a 2-D float32 tensor on the inputs' device")
+    if src1.stride(1) != 1 and src1.size(1) > 1:
+        raise ValueError("src1 must have unit stride along its last dimension")
+    m = int(src1.size(0) if src1_transposed else src1.size(1))
+    k_dim = int(src1.size(1) if src1_transposed else src1.size(0))
+    if k_dim != n_rows:
+        raise ValueError(f"src1 has {k_dim} rows of the summed dimension, the weight {n_rows}")
+    ld = max(int(src1.stride(0)), 1)
+    if dst is None:
+        dst = torch.empty((m, n_cols), dtype=torch.float32, device=device)
+    elif (dst.device != device or dst.dtype != torch.float32 or not dst.is_contiguous()
+          or dst.numel() < m * n_cols):
+        raise ValueError("dst must be a contiguous float32 tensor of m * n_cols values")
+    if workspace is None:
+        rows = max(1, min(n_rows, int(workspace_bytes) // max(4 * n_cols, 1)))
+        workspace = torch.empty(max(rows * n_cols, 1), dtype=torch.float32, device=device)
+    elif (workspace.device != device or workspace.dtype != torch.float32
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 tensor on the inputs' device")
+    with torch.cuda.device(device):
+        st = library().dq4_out_prod_rows(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), n_rows,
+            n_cols, int(blocksize), int(nested_blocksize), src1.data_ptr(), m, ld,
+            1 if src1_transposed else 0, dst.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * 4, _stream_handle(device, stream))
+    _raise_for(st, "dq4_out_prod_rows")
+    return dst
 
 
 def to_device(x, device="cuda"):

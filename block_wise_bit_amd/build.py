@@ -19,7 +19,9 @@ import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "dq4.hip"), os.path.join(PKG, "csrc", "dq4_unfused.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name)
+           for name in ("dq4.hip", "dq4_unfused.hip", "dq4_out_prod.hip")]
+LIBS = ["-lrocblas"]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdq4.so")
 KERNEL_DIGESTS = os.path.join(PKG, "libdq4_kernels.json")  # written next to the library
@@ -45,7 +47,8 @@ def hipcc() -> str:
 def build(out: str = LIBRARY, extra_flags=()) -> str:
     """Compile the library; always recompiles.  Returns the .so path."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-shared", "-I", INCLUDE, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-shared", "-I", INCLUDE, "-o", tmp, *SOURCES,
+           *LIBS]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     with tempfile.TemporaryDirectory() as d:

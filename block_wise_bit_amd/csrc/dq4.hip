@@ -374,6 +374,8 @@ const char *dq4_status_string(dq4_status_t status)
         return "DQ4_EUNSUPPORTED: unsupported block layout";
     case DQ4_EHIP:
         return "DQ4_EHIP: kernel launch failed";
+    case DQ4_EBLAS:
+        return "DQ4_EBLAS: library GEMM failed";
     default:
         return "DQ4: unknown status";
     }

@@ -64,7 +64,8 @@ enum {
                               row window, unknown output type */
     DQ4_EUNSUPPORTED = 2,  /* blocksize not a power of two in [32, 4096], or
                               nested_blocksize other than 256 */
-    DQ4_EHIP = 3           /* the kernel launch failed */
+    DQ4_EHIP = 3,          /* the kernel launch failed */
+    DQ4_EBLAS = 4          /* the library GEMM (rocBLAS) failed */
 };
 
 enum {
@@ -141,6 +142,43 @@ dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *sc
 /* Bytes of FP32 scale workspace dq4_nested_dequant_unfused needs: 4 * ceil(n /
  * blocksize); 0 for non-positive arguments.  Host only. */
 int64_t dq4_unfused_workspace_bytes(int64_t n, int32_t blocksize);
+
+/*
+ * Row-blocked out_prod of a nested 4-bit weight (llama.cpp PR "cuda: out_prod
+ * dequantizes a 2D weight in row blocks", section "What" and the review):
+ *
+ *     dst[i][j] = sum over r in [0, n_rows) of B[r][i] * W[r][j]
+ *
+ * W is the n_rows x n_cols nested 4-bit weight described by the first ten
+ * arguments (as for dq4_nested_dequant_rows).  B is src1, FP32 device memory:
+ *   src1_transposed == 0: B[r][i] = src1[r * ld_src1 + i]   (stored n_rows x m, ld_src1 >= m)
+ *   src1_transposed == 1: B[r][i] = src1[i * ld_src1 + r]   (stored m x n_rows, ld_src1 >= n_rows)
+ * dst: m x n_cols FP32 row-major device memory, overwritten (n_rows == 0
+ * writes zeros).  workspace: caller-owned device buffer of workspace_bytes
+ * bytes, at least one F32 row (n_cols * 4); the weight is dequantized to F32
+ * in consecutive windows of dq4_rows_per_block(n_cols, 4, workspace_bytes)
+ * rows into it, and for each window an FP32 GEMM (rocBLAS) adds
+ * B[r0:r0+rows]^T * window into dst, with beta 0 for the first window and 1
+ * after -- the same sum as one GEMM over the whole dequantized weight.
+ *
+ * Everything is enqueued on `stream`; nothing is synchronized.  The first
+ * call on a thread and device creates a rocBLAS handle for it (rocBLAS
+ * manages that handle's own device memory); nothing else is allocated.
+ * Returns DQ4_EBLAS (code in dq4_last_blas_status()) if rocBLAS fails,
+ * DQ4_EINVAL for bad sizes, a leading dimension that is too small or a
+ * workspace smaller than one row, or any size above 2^31 - 1 that rocBLAS's
+ * 32-bit interface cannot take.
+ */
+dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes,
+                               const float *nested_absmax, const float *scale_codebook,
+                               const float *codebook4, float offset, int64_t n_rows,
+                               int64_t n_cols, int32_t blocksize, int32_t nested_blocksize,
+                               const float *src1, int64_t m, int64_t ld_src1,
+                               int32_t src1_transposed, float *dst, float *workspace,
+                               int64_t workspace_bytes, void *stream);
+
+/* rocBLAS status of this thread's last DQ4_EBLAS, 0 if none. */
+int32_t dq4_last_blas_status(void);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *dq4_status_string(dq4_status_t status);

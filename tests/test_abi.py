@@ -25,7 +25,8 @@ def test_exports_every_declared_function(lib):
     names = dq4.header_functions()
     assert set(names) == {"dq4_nested_dequant", "dq4_nested_dequant_rows", "dq4_rows_per_block",
                           "dq4_status_string", "dq4_last_hip_error",
-                          "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes"}
+                          "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
+                          "dq4_out_prod_rows", "dq4_last_blas_status"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -34,10 +35,11 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for st in (dq4.DQ4_OK, dq4.DQ4_EINVAL, dq4.DQ4_EUNSUPPORTED, dq4.DQ4_EHIP, 99):
+    for st in (dq4.DQ4_OK, dq4.DQ4_EINVAL, dq4.DQ4_EUNSUPPORTED, dq4.DQ4_EHIP, dq4.DQ4_EBLAS, 99):
         s = dq4.dq4_status_string(st)
         assert s.startswith("DQ4")
     assert dq4.dq4_last_hip_error() == 0
+    assert dq4.dq4_last_blas_status() == 0
 
 
 def _call(lib, n=64, blocksize=64, nested=256, dtype=dq4.DQ4_F16, ptr=1, out=1):
@@ -78,6 +80,28 @@ def test_validation_unfused(lib):
     assert dq4.dq4_unfused_workspace_bytes(1024, 64) == 4 * 16
     assert dq4.dq4_unfused_workspace_bytes(1025, 64) == 4 * 17
     assert dq4.dq4_unfused_workspace_bytes(0, 64) == 0
+
+
+def test_validation_out_prod(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(n_rows=100, n_cols=64, m=8, ld=8, trans=0, ws_bytes=64 * 4 * 10, blocksize=64,
+             ws=p, src=p, dst=p):
+        return lib.dq4_out_prod_rows(p, p, p, p, p, ctypes.c_float(0.0), n_rows, n_cols, blocksize,
+                                     256, src, m, ld, trans, dst, ws, ws_bytes, None)
+    assert call(m=0) == dq4.DQ4_OK                    # empty dst: nothing to do
+    assert call(n_cols=0) == dq4.DQ4_OK
+    assert call(n_rows=-1) == dq4.DQ4_EINVAL
+    assert call(m=-1) == dq4.DQ4_EINVAL
+    assert call(trans=2) == dq4.DQ4_EINVAL
+    assert call(ld=7) == dq4.DQ4_EINVAL               # ld < m
+    assert call(trans=1, ld=99) == dq4.DQ4_EINVAL     # ld < n_rows
+    assert call(ws_bytes=64 * 4 - 1) == dq4.DQ4_EINVAL  # less than one F32 row
+    assert call(ws=None) == dq4.DQ4_EINVAL
+    assert call(src=None) == dq4.DQ4_EINVAL
+    assert call(dst=None) == dq4.DQ4_EINVAL
+    assert call(m=1 << 31, ld=1 << 31) == dq4.DQ4_EINVAL   # beyond the 32-bit GEMM interface
+    assert call(blocksize=7) == dq4.DQ4_EUNSUPPORTED
 
 
 def _call_rows(lib, n_rows=10, n_cols=64, r0=0, rows=1, blocksize=64, dtype=dq4.DQ4_F32, ptr=1):

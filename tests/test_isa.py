@@ -41,7 +41,8 @@ def test_kernels_present(asm):
     names = list(_kernel_bodies(asm))
     for kernel, count in (("dq4_tile_kernel", 3), ("dq4_elem_kernel", 3),
                           ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
-                          ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1)):
+                          ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
+                          ("zero_fill_kernel", 1)):
         assert sum(kernel in n for n in names) == count, kernel
 
 
@@ -51,7 +52,7 @@ def test_no_fused_or_packed_fp_instructions(asm):
         assert not found, f"{name}: {found}"
         if "add_offset" in name:
             assert "v_add_f32" in code, name
-        else:
+        elif "zero_fill" not in name:
             assert "v_mul_f32" in code, name
         if "dq4_tile_kernel" in name or "dq4_elem_kernel" in name:
             assert "v_add_f32" in code, name   # the scale is rebuilt in the fused kernels
