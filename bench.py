@@ -303,6 +303,76 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
     return 0
 
 
+def linear_bench(args, torch, dq4, inputs) -> int:
+    """Dequantize-plus-linear cells (the issue's public-path controls: the
+    forward fallback Y = X W^T and MatMul4Bit grad_A Y = G W) for two weight
+    shapes and several token counts m.  Each cell times the whole call
+    (fused dequantization + one GEMM), the fused dequantization alone, and the
+    unfused three-launch dequantization alone; the GEMM is the same in both
+    paths, so the public-path effect of the fusion is
+    (t_call - t_fused + t_unfused) / t_call."""
+    import math
+
+    def timeit(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps  # us
+
+    cells = []
+    for n_out, n_in in ((11008, 4096), (28672, 8192)):
+        x = inputs.make_inputs(n_out * n_in, 64, "nf4", 0.03, seed=inputs.SEED_BASE + 6,
+                               n_rows=n_out, n_cols=n_in)
+        dev = dq4.to_device(x, "cuda:0")
+        for dt in (torch.float16, torch.bfloat16):
+            ws = torch.empty(n_out * n_in, dtype=dt, device="cuda:0")
+            sw = torch.empty(dq4.dq4_unfused_workspace_bytes(n_out * n_in, 64) // 4,
+                             dtype=torch.float32, device="cuda:0")
+            t_fused = timeit(lambda: dq4.dq4_nested_dequant(
+                **dev, offset=float(x.offset), n=n_out * n_in, blocksize=64, out_dtype=dt,
+                out=ws))
+            t_unfused = timeit(lambda: dq4.dq4_nested_dequant_unfused(
+                **dev, offset=float(x.offset), n=n_out * n_in, blocksize=64, out_dtype=dt,
+                out=ws, scale_workspace=sw))
+            for op in ("forward", "grad_a"):
+                for m in (1, 16, 512, 4096):
+                    k = n_in if op == "forward" else n_out
+                    xin = torch.randn((m, k), device="cuda:0").to(dt)
+                    y = torch.empty((m, n_out if op == "forward" else n_in), dtype=dt,
+                                    device="cuda:0")
+                    t_call = timeit(lambda: dq4.dq4_dequant_linear(
+                        **dev, offset=float(x.offset), n_out=n_out, n_in=n_in, blocksize=64,
+                        x=xin, op=op, y=y, w_workspace=ws))
+                    flops = 2.0 * m * n_out * n_in
+                    cell = {"weight": f"{n_out}x{n_in}", "dtype": str(dt).split(".")[-1],
+                            "op": op, "m": m, "call_us": round(t_call, 2),
+                            "fused_dequant_us": round(t_fused, 2),
+                            "unfused_dequant_us": round(t_unfused, 2),
+                            "gemm_us": round(max(t_call - t_fused, 0.0), 2),
+                            "gemm_TFLOPs": round(flops / max(t_call - t_fused, 1e-3) / 1e6, 2),
+                            "public_path_speedup": round((t_call - t_fused + t_unfused) / t_call,
+                                                         4)}
+                    cells.append(cell)
+                    print(f"[linear] {cell}", file=sys.stderr, flush=True)
+            del ws, sw
+        del dev
+        torch.cuda.empty_cache()
+    sp = [c["public_path_speedup"] for c in cells]
+    print(json.dumps({
+        "metric": "dequantize-plus-linear public-path speedup of the fused dequantization "
+                  "(geomean over forward/grad_A cells)",
+        "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 4), "unit": "x",
+        "higher_is_better": True, "n_gpus": 1, "data": "synthetic", "cells": cells,
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +391,9 @@ def main() -> int:
                          "151936x5376 output head (FP32 GEMM per window)")
     ap.add_argument("--out-prod-m", type=int, default=512,
                     help="columns of src1 (tokens) for --out-prod")
+    ap.add_argument("--linear", action="store_true",
+                    help="instead of the benchmark, time dequantize-plus-linear forward and "
+                         "grad_A cells")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of MIB "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -348,6 +421,8 @@ def main() -> int:
         return compare_unfused(args, torch, dq4, inputs)
     if args.out_prod:
         return out_prod_bench(args, torch, dq4, inputs)
+    if args.linear:
+        return linear_bench(args, torch, dq4, inputs)
 
     wl = inputs.HEADLINE
     n, bs = wl.n, wl.blocksize

@@ -16,6 +16,8 @@ cannot be loaded, every call raises.
     dq4_unfused_workspace_bytes(n, blocksize) -> int
     dq4_out_prod_rows(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
                                                    (row-blocked out_prod, FP32 GEMM)
+    dq4_dequant_linear(..., n_out, n_in, blocksize, x, op) -> tensor
+                                                   (Y = X W^T or G W, FP16/BF16 GEMM)
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "dq4.h")
 
 DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP, DQ4_EBLAS = 0, 1, 2, 3, 4
 DQ4_F32, DQ4_F16, DQ4_BF16 = 0, 1, 2
+DQ4_LINEAR_FORWARD, DQ4_LINEAR_GRAD_A = 0, 1
 NESTED_BLOCKSIZE = 256
 ROW_BLOCK_BUDGET_BYTES = 256 << 20   # 256 MiB of F32 per transient row block
 
@@ -66,6 +69,9 @@ def library() -> ctypes.CDLL:
     lib.dq4_out_prod_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, P, i64, i64, i32, P,
                                       P, i64, P]
     lib.dq4_out_prod_rows.restype = i32
+    lib.dq4_dequant_linear.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, i32, i32, P, i64,
+                                       P, P, P]
+    lib.dq4_dequant_linear.restype = i32
     lib.dq4_last_blas_status.argtypes = []
     lib.dq4_last_blas_status.restype = i32
     lib.dq4_status_string.argtypes = [i32]
@@ -318,6 +324,48 @@ def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebo
             workspace.numel() * 4, _stream_handle(device, stream))
     _raise_for(st, "dq4_out_prod_rows")
     return dst
+
+
+def dq4_dequant_linear(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                       offset: float, n_out: int, n_in: int, blocksize: int, x,
+                       op: str = "forward", y=None, w_workspace=None,
+                       nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
+    """Dequantize the n_out x n_in weight W whole (into w_workspace, allocated
+    when None) and run one GEMM: op "forward" gives Y = X W^T (x: m x n_in),
+    op "grad_a" gives Y = G W (x: m x n_out).  x's dtype (float16 or
+    bfloat16) is the dtype of W and Y.  Returns Y."""
+    torch = _torch()
+    n_out, n_in = int(n_out), int(n_in)
+    ops = {"forward": DQ4_LINEAR_FORWARD, "grad_a": DQ4_LINEAR_GRAD_A}
+    if op not in ops:
+        raise ValueError("op must be 'forward' or 'grad_a'")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    code = _out_code(x.dtype)
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           n_out * n_in, int(blocksize), int(nested_blocksize))
+    k = n_in if op == "forward" else n_out
+    width = n_out if op == "forward" else n_in
+    if x.device != device or x.dim() != 2 or x.size(1) != k or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous (m, {k}) tensor on the inputs' device")
+    m = int(x.size(0))
+    if y is None:
+        y = torch.empty((m, width), dtype=x.dtype, device=device)
+    elif y.device != device or y.dtype != x.dtype or not y.is_contiguous() or y.numel() < m * width:
+        raise ValueError(f"y must be a contiguous {x.dtype} tensor of {m} x {width} values")
+    if w_workspace is None:
+        w_workspace = torch.empty(max(n_out * n_in, 1), dtype=x.dtype, device=device)
+    elif (w_workspace.device != device or w_workspace.dtype != x.dtype
+          or not w_workspace.is_contiguous() or w_workspace.numel() < n_out * n_in):
+        raise ValueError("w_workspace must hold n_out * n_in values of x's dtype")
+    with torch.cuda.device(device):
+        st = library().dq4_dequant_linear(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), n_out,
+            n_in, int(blocksize), int(nested_blocksize), code, ops[op], x.data_ptr(), m,
+            y.data_ptr(), w_workspace.data_ptr(), _stream_handle(device, stream))
+    _raise_for(st, "dq4_dequant_linear")
+    return y
 
 
 def to_device(x, device="cuda"):

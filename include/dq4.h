@@ -74,6 +74,11 @@ enum {
     DQ4_BF16 = 2
 };
 
+enum {
+    DQ4_LINEAR_FORWARD = 0,  /* Y = X W^T */
+    DQ4_LINEAR_GRAD_A = 1    /* Y = G W   */
+};
+
 /*
  * Whole-tensor dequantization of n elements (the fused nested dequantization
  * of the bitsandbytes issue above, section "Proposed experiment").
@@ -176,6 +181,30 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
                                const float *src1, int64_t m, int64_t ld_src1,
                                int32_t src1_transposed, float *dst, float *workspace,
                                int64_t workspace_bytes, void *stream);
+
+/*
+ * Dequantize-plus-linear (bitsandbytes issue above, section "Problem": the
+ * dequantize-plus-linear fallback that materializes the full weight before
+ * F.linear, and MatMul4Bit.backward's grad_A, which uses the same
+ * dequantization).  W is the n_out x n_in nested 4-bit weight (row-major,
+ * first ten arguments as for dq4_nested_dequant with n = n_out * n_in).  It is
+ * dequantized whole into w_workspace (n_out * n_in elements of `dtype`,
+ * caller-owned device memory; bit-identical to dq4_nested_dequant), then one
+ * GEMM (rocBLAS, FP32 accumulation, inputs and output in `dtype`):
+ *   op == DQ4_LINEAR_FORWARD:  Y[i][o] = sum_k X[i][k] W[o][k]   x: m x n_in,  y: m x n_out
+ *   op == DQ4_LINEAR_GRAD_A:   Y[i][k] = sum_o X[i][o] W[o][k]   x: m x n_out, y: m x n_in
+ * x and y are dense row-major device arrays of `dtype` (DQ4_F16 or DQ4_BF16).
+ * Everything is enqueued on `stream`.  An empty Y (m or its width 0) is a
+ * no-op.  Sizes above 2^31 - 1 are DQ4_EINVAL (rocBLAS's 32-bit interface);
+ * rocBLAS failures are DQ4_EBLAS.  The rocBLAS handle is as for
+ * dq4_out_prod_rows.
+ */
+dq4_status_t dq4_dequant_linear(const uint8_t *packed, const uint8_t *scale_codes,
+                                const float *nested_absmax, const float *scale_codebook,
+                                const float *codebook4, float offset, int64_t n_out,
+                                int64_t n_in, int32_t blocksize, int32_t nested_blocksize,
+                                int32_t dtype, int32_t op, const void *x, int64_t m, void *y,
+                                void *w_workspace, void *stream);
 
 /* rocBLAS status of this thread's last DQ4_EBLAS, 0 if none. */
 int32_t dq4_last_blas_status(void);

@@ -26,7 +26,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"dq4_nested_dequant", "dq4_nested_dequant_rows", "dq4_rows_per_block",
                           "dq4_status_string", "dq4_last_hip_error",
                           "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
-                          "dq4_out_prod_rows", "dq4_last_blas_status"}
+                          "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -102,6 +102,24 @@ def test_validation_out_prod(lib):
     assert call(dst=None) == dq4.DQ4_EINVAL
     assert call(m=1 << 31, ld=1 << 31) == dq4.DQ4_EINVAL   # beyond the 32-bit GEMM interface
     assert call(blocksize=7) == dq4.DQ4_EUNSUPPORTED
+
+
+def test_validation_linear(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(n_out=64, n_in=64, m=4, dtype=dq4.DQ4_F16, op=0, x=p, y=p, ws=p, blocksize=64):
+        return lib.dq4_dequant_linear(p, p, p, p, p, ctypes.c_float(0.0), n_out, n_in, blocksize,
+                                      256, dtype, op, x, m, y, ws, None)
+    assert call(m=0) == dq4.DQ4_OK
+    assert call(n_out=0, op=0) == dq4.DQ4_OK          # forward: Y is m x 0
+    assert call(n_in=0, op=1) == dq4.DQ4_OK           # grad_A: Y is m x 0
+    assert call(dtype=dq4.DQ4_F32) == dq4.DQ4_EINVAL
+    assert call(op=2) == dq4.DQ4_EINVAL
+    assert call(m=-1) == dq4.DQ4_EINVAL
+    assert call(x=None) == dq4.DQ4_EINVAL
+    assert call(ws=None) == dq4.DQ4_EINVAL
+    assert call(n_out=1 << 31) == dq4.DQ4_EINVAL
+    assert call(blocksize=16) == dq4.DQ4_EUNSUPPORTED
 
 
 def _call_rows(lib, n_rows=10, n_cols=64, r0=0, rows=1, blocksize=64, dtype=dq4.DQ4_F32, ptr=1):
