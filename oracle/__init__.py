@@ -31,6 +31,14 @@ Pins (what the oracle is checked against, in ``tests/test_oracle_pins.py``):
     must each fail a pin.
 Parity unpinned: the upstream library's own NF4/FP4 tables and nibble order
 (the pages print neither; the tables are inputs here) and NaN payloads.
+
+``int8_prep_oracle.c`` is the oracle of the LLM.int8 correction-operand
+preparation (bitsandbytes issue "Fuse LLM.int8 correction operand preparation
+into one CUDA kernel"), pinned in ``tests/test_int8_prep_pins.py`` against
+the exact-rational model over the whole int8 code domain and zero, normal,
+subnormal-adjacent and large finite row scales, and against numpy indexing for
+the gathers.  Parity unpinned: the digits of the upstream reciprocal-127
+constant (read as the FP32 value nearest 1/127).
 """
 from __future__ import annotations
 
@@ -64,6 +72,8 @@ class OracleLib:
         lib.dq4o_f32_to_f16_array.restype = None
         lib.dq4o_f32_to_bf16_array.argtypes = [P, P, i64]
         lib.dq4o_f32_to_bf16_array.restype = None
+        lib.dq4o_int8_prep.argtypes = [P, i64, i64, P, P, i64, P, i64, P, P]
+        lib.dq4o_int8_prep.restype = ctypes.c_int
         self.path = path
         self.lib = lib
 
@@ -186,3 +196,25 @@ def f32_to_bf16_bits(bits_u32: np.ndarray, oracle: OracleLib | None = None) -> n
     out = np.empty(a.size, dtype=np.uint16)
     lib.dq4o_f32_to_bf16_array(_ptr(a), _ptr(out), a.size)
     return out
+
+
+def int8_prep(A_bits: np.ndarray, CB: np.ndarray, SCB: np.ndarray, cols: np.ndarray,
+              oracle: OracleLib | None = None):
+    """LLM.int8 correction operands: subA (M x L, A's raw 16-bit values) and
+    subB (L x N, FP16 bits) -- see int8_prep_oracle.c."""
+    lib = (oracle or load()).lib
+    A_bits = _c(A_bits, np.uint16)
+    CB = _c(CB, np.int8)
+    SCB = _c(SCB, np.float32)
+    cols = _c(cols, np.int64)
+    M, K = A_bits.shape
+    N = CB.shape[0]
+    assert CB.shape == (N, K) and SCB.shape == (N,)
+    L = cols.size
+    subA = np.empty((M, L), np.uint16)
+    subB = np.empty((L, N), np.uint16)
+    rc = lib.dq4o_int8_prep(_ptr(A_bits), M, K, _ptr(CB), _ptr(SCB), N, _ptr(cols), L,
+                            _ptr(subA), _ptr(subB))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return subA, subB

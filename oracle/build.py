@@ -12,6 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "dq4_oracle.c")
+EXTRA_SOURCES = [os.path.join(HERE, "int8_prep_oracle.c")]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
@@ -22,12 +23,15 @@ def library_path(build_dir: str = BUILD_DIR) -> str:
     return os.path.join(build_dir, "libdq4_oracle.so")
 
 
-def build(source: str = SOURCE, build_dir: str = BUILD_DIR, extra_flags=()) -> str:
-    """Compile `source` into build_dir/libdq4_oracle.so and return its path."""
+def build(source: str = SOURCE, build_dir: str = BUILD_DIR, extra_flags=(),
+          extra_sources=None) -> str:
+    """Compile `source` (and the other oracle sources) into
+    build_dir/libdq4_oracle.so and return its path."""
     os.makedirs(build_dir, exist_ok=True)
     out = library_path(build_dir)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, source]
+    others = EXTRA_SOURCES if extra_sources is None else extra_sources
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, source, *others]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

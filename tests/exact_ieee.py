@@ -60,8 +60,12 @@ def _to_float(r, negative: bool) -> float:
 
 
 def mul32(a: float, b: float) -> float:
-    """fl32(a * b) for finite binary32 a, b."""
+    """fl32(a * b) for binary32 a, b (infinities allowed, NaN not)."""
     negative = _signbit(a) != _signbit(b)
+    if math.isinf(a) or math.isinf(b):
+        if a == 0 or b == 0:
+            return math.nan
+        return -math.inf if negative else math.inf
     exact = Fraction(a) * Fraction(b)
     if exact == 0:
         return -0.0 if negative else 0.0
@@ -86,6 +90,8 @@ def _encode_narrow(x: float, fmt, frac_bits: int, exp_bias: int) -> int:
     r = round_rne(abs(Fraction(x)), fmt)
     if r is None:
         return sign | (((1 << (15 - frac_bits)) - 1) << frac_bits)
+    if r == 0:  # below half the smallest subnormal: a signed zero
+        return sign
     p, emin, _ = fmt
     e = _floor_log2(r)
     if e < emin:  # subnormal: integer multiple of the subnormal quantum
