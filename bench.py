@@ -373,6 +373,76 @@ def linear_bench(args, torch, dq4, inputs) -> int:
     return 0
 
 
+def int8_prep_bench(args, torch, dq4) -> int:
+    """One-launch LLM.int8 correction-operand preparation against the eager
+    PyTorch chain it replaces (gather, int8 row-scale dequantization, FP16
+    conversion, transposed copy), over the issue's benchmark grid: M in {1, 8,
+    64, 512, 2048}, K = N in {3584, 4096, 8192, 14336}, L in {1, 5, 16, 64}."""
+    import math
+
+    r127 = 7.874015718698502e-3   # float(np.float32(1/127)): the FP32 value nearest 1/127
+
+    def timeit(fn, reps=50):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    g = torch.Generator(device="cuda:0").manual_seed(3)
+    cells = []
+    for K in (3584, 4096, 8192, 14336):
+        N = K
+        CB = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda:0", generator=g)
+        SCB = torch.rand(N, device="cuda:0", generator=g) * 10
+        for M in (1, 8, 64, 512, 2048):
+            A = torch.randn((M, K), device="cuda:0", generator=g).half()
+            for L in (1, 5, 16, 64):
+                cols = torch.randperm(K, device="cuda:0", generator=g)[:L].sort().values
+                subA = torch.empty((M, L), dtype=torch.float16, device="cuda:0")
+                subB = torch.empty((L, N), dtype=torch.float16, device="cuda:0")
+                lib = dq4.library()
+                stream = torch.cuda.current_stream().cuda_stream
+
+                def fused():
+                    lib.dq4_int8_prep(A.data_ptr(), M, K, CB.data_ptr(), SCB.data_ptr(), N,
+                                      cols.data_ptr(), L, subA.data_ptr(), subB.data_ptr(),
+                                      stream)
+
+                def eager():
+                    ea = A[:, cols].contiguous()
+                    eb = (CB[:, cols].contiguous() * SCB.view(-1, 1) * r127).to(
+                        torch.float16).t().contiguous()
+                    return ea, eb
+
+                t_f = timeit(fused)
+                t_e = timeit(eager)
+                ea, eb = eager()
+                fused()
+                torch.cuda.synchronize()
+                same = bool(torch.equal(ea.view(torch.int16), subA.view(torch.int16)) and
+                            torch.equal(eb.view(torch.int16), subB.view(torch.int16)))
+                cells.append({"M": M, "K": K, "N": N, "L": L, "fused_us": round(t_f, 2),
+                              "eager_us": round(t_e, 2), "speedup": round(t_e / t_f, 3),
+                              "bit_equal_to_eager": same})
+                print(f"[int8] {cells[-1]}", file=sys.stderr, flush=True)
+    sp = [c["speedup"] for c in cells]
+    print(json.dumps({
+        "metric": "LLM.int8 correction-operand preparation: one kernel vs the eager chain "
+                  "(speedup, geomean)",
+        "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 3), "unit": "x",
+        "higher_is_better": True, "min_speedup": min(sp), "median_speedup": sorted(sp)[len(sp) // 2],
+        "all_bit_equal": all(c["bit_equal_to_eager"] for c in cells), "n_gpus": 1,
+        "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0)}),
+        flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +464,9 @@ def main() -> int:
     ap.add_argument("--linear", action="store_true",
                     help="instead of the benchmark, time dequantize-plus-linear forward and "
                          "grad_A cells")
+    ap.add_argument("--int8-prep", action="store_true",
+                    help="instead of the benchmark, time the LLM.int8 correction-operand "
+                         "preparation against the eager chain")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of MIB "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -423,6 +496,8 @@ def main() -> int:
         return out_prod_bench(args, torch, dq4, inputs)
     if args.linear:
         return linear_bench(args, torch, dq4, inputs)
+    if args.int8_prep:
+        return int8_prep_bench(args, torch, dq4)
 
     wl = inputs.HEADLINE
     n, bs = wl.n, wl.blocksize

@@ -18,6 +18,7 @@ cannot be loaded, every call raises.
                                                    (row-blocked out_prod, FP32 GEMM)
     dq4_dequant_linear(..., n_out, n_in, blocksize, x, op) -> tensor
                                                    (Y = X W^T or G W, FP16/BF16 GEMM)
+    dq4_int8_prep(A, CB, SCB, cols) -> (subA, subB)  (LLM.int8 correction operands)
 """
 from __future__ import annotations
 
@@ -72,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.dq4_dequant_linear.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, i32, i32, P, i64,
                                        P, P, P]
     lib.dq4_dequant_linear.restype = i32
+    lib.dq4_int8_prep.argtypes = [P, i64, i64, P, P, i64, P, i64, P, P, P]
+    lib.dq4_int8_prep.restype = i32
     lib.dq4_last_blas_status.argtypes = []
     lib.dq4_last_blas_status.restype = i32
     lib.dq4_status_string.argtypes = [i32]
@@ -366,6 +369,49 @@ def dq4_dequant_linear(packed, scale_codes, nested_absmax, scale_codebook, codeb
             y.data_ptr(), w_workspace.data_ptr(), _stream_handle(device, stream))
     _raise_for(st, "dq4_dequant_linear")
     return y
+
+
+def dq4_int8_prep(A, CB, SCB, cols, subA=None, subB=None, stream=None):
+    """LLM.int8 correction operands in one kernel: subA = A[:, cols] (M x L,
+    FP16) and subB = fp16(fl32(fl32(CB[:, cols] * SCB[:, None]) * R127)).T
+    (L x N, FP16, contiguous).  Column indices are checked here (a host
+    synchronization) and out-of-range ones raise ValueError."""
+    torch = _torch()
+    device = A.device
+    if device.type != "cuda":
+        raise ValueError("A must be a GPU tensor")
+    if A.dtype != torch.float16 or A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous 2-D float16 tensor")
+    if CB.dtype != torch.int8 or CB.dim() != 2 or not CB.is_contiguous():
+        raise ValueError("CB must be a contiguous 2-D int8 tensor")
+    if SCB.dtype != torch.float32 or SCB.dim() != 1 or not SCB.is_contiguous():
+        raise ValueError("SCB must be a contiguous 1-D float32 tensor")
+    if cols.dtype != torch.int64 or cols.dim() != 1 or not cols.is_contiguous():
+        raise ValueError("cols must be a contiguous 1-D int64 tensor")
+    for name, t in (("CB", CB), ("SCB", SCB), ("cols", cols)):
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+    M, K = A.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.numel() != N:
+        raise ValueError(f"CB must be N x {K} and SCB must hold N values")
+    L = cols.numel()
+    if L and bool(((cols < 0) | (cols >= K)).any()):
+        raise ValueError(f"column indices must lie in [0, {K})")
+    if subA is None:
+        subA = torch.empty((M, L), dtype=torch.float16, device=device)
+    if subB is None:
+        subB = torch.empty((L, N), dtype=torch.float16, device=device)
+    for name, t, numel in (("subA", subA, M * L), ("subB", subB, L * N)):
+        if (t.device != device or t.dtype != torch.float16 or not t.is_contiguous()
+                or t.numel() < numel):
+            raise ValueError(f"{name} must be a contiguous float16 tensor of {numel} values")
+    with torch.cuda.device(device):
+        st = library().dq4_int8_prep(A.data_ptr(), M, K, CB.data_ptr(), SCB.data_ptr(), N,
+                                     cols.data_ptr(), L, subA.data_ptr(), subB.data_ptr(),
+                                     _stream_handle(device, stream))
+    _raise_for(st, "dq4_int8_prep")
+    return subA, subB
 
 
 def to_device(x, device="cuda"):

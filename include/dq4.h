@@ -206,6 +206,29 @@ dq4_status_t dq4_dequant_linear(const uint8_t *packed, const uint8_t *scale_code
                                 int32_t dtype, int32_t op, const void *x, int64_t m, void *y,
                                 void *w_workspace, void *stream);
 
+/*
+ * LLM.int8 correction-operand preparation in one kernel (bitsandbytes issue
+ * "Fuse LLM.int8 correction operand preparation into one CUDA kernel",
+ * sections "Bounded method" and "Exact correctness oracle"):
+ *     subA[r][l] = A[r][cols[l]]                                  r < M, l < L
+ *     subB[l][n] = fp16(fl32(fl32(CB[n][cols[l]] * SCB[n]) * R127))  n < N
+ * A: M x K FP16 (16-bit values, copied bit for bit), CB: N x K int8, SCB: N
+ * FP32 row scales, cols: L int64 column indices (any order, repeats allowed),
+ * all dense row-major device arrays.  subA: M x L and subB: L x N (the
+ * transposed layout the correction GEMM consumes), FP16, caller-owned.
+ * R127 is the FP32 value nearest 1/127; the multiply by the row scale and the
+ * multiply by R127 are separately rounded FP32 operations, and the FP16
+ * conversion is round-to-nearest-even.  One kernel on `stream`; L == 0 (no
+ * outlier columns) launches nothing and returns DQ4_OK.  A column index
+ * outside [0, K) is not read: the outputs it feeds are set to FP16 NaN
+ * (0x7E00).  DQ4_EINVAL for negative sizes, K == 0 with L > 0, or a null
+ * pointer an output needs; DQ4_EUNSUPPORTED when M*K, N*K or (M+N)*L reaches
+ * 2^31 - 2^24 (the kernel indexes in 32 bits).
+ */
+dq4_status_t dq4_int8_prep(const uint16_t *A, int64_t M, int64_t K, const int8_t *CB,
+                           const float *SCB, int64_t N, const int64_t *cols, int64_t L,
+                           uint16_t *subA, uint16_t *subB, void *stream);
+
 /* rocBLAS status of this thread's last DQ4_EBLAS, 0 if none. */
 int32_t dq4_last_blas_status(void);
 

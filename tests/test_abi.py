@@ -26,7 +26,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"dq4_nested_dequant", "dq4_nested_dequant_rows", "dq4_rows_per_block",
                           "dq4_status_string", "dq4_last_hip_error",
                           "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
-                          "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear"}
+                          "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear",
+                          "dq4_int8_prep"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -120,6 +121,24 @@ def test_validation_linear(lib):
     assert call(ws=None) == dq4.DQ4_EINVAL
     assert call(n_out=1 << 31) == dq4.DQ4_EINVAL
     assert call(blocksize=16) == dq4.DQ4_EUNSUPPORTED
+
+
+def test_validation_int8_prep(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(M=4, K=64, N=8, L=2, A=p, CB=p, SCB=p, cols=p, subA=p, subB=p):
+        return lib.dq4_int8_prep(A, M, K, CB, SCB, N, cols, L, subA, subB, None)
+    assert call(L=0) == dq4.DQ4_OK                    # the empty-outlier path: nothing launched
+    assert call(L=0, A=None, CB=None, cols=None) == dq4.DQ4_OK
+    assert call(M=0, N=0) == dq4.DQ4_OK
+    assert call(M=-1) == dq4.DQ4_EINVAL
+    assert call(L=-1) == dq4.DQ4_EINVAL
+    assert call(K=0) == dq4.DQ4_EINVAL
+    assert call(cols=None) == dq4.DQ4_EINVAL
+    assert call(subA=None) == dq4.DQ4_EINVAL
+    assert call(subB=None) == dq4.DQ4_EINVAL
+    assert call(M=1 << 40, K=1 << 40) == dq4.DQ4_EINVAL   # overflows 64 bits
+    assert call(M=1 << 20, K=1 << 12) == dq4.DQ4_EUNSUPPORTED   # beyond 32-bit indexing
 
 
 def _call_rows(lib, n_rows=10, n_cols=64, r0=0, rows=1, blocksize=64, dtype=dq4.DQ4_F32, ptr=1):

@@ -42,7 +42,7 @@ def test_kernels_present(asm):
     for kernel, count in (("dq4_tile_kernel", 3), ("dq4_elem_kernel", 3),
                           ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
-                          ("zero_fill_kernel", 1)):
+                          ("zero_fill_kernel", 1), ("int8_prep_kernel", 1)):
         assert sum(kernel in n for n in names) == count, kernel
 
 
