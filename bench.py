@@ -447,7 +447,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=700, help="timed steps (split into 7 batches)")
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (>= 20; the default lets clocks settle)")
     ap.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled")
     ap.add_argument("--batches", type=int, default=7)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

@@ -14,7 +14,7 @@
 // traffic of the FP32 buffer (4 B written, 4 B read + 4 B written, 4 B read
 // per block) and two extra launches -- the cost the fusion removes.
 //
-// Launch 3 has the same tile structure as the fused kernel (256 lanes, 8192
+// Launch 3 has the same tile structure as the fused kernel (256 lanes, 4096
 // elements per workgroup, streaming stores), so the comparison measures the
 // fusion and nothing else.
 
@@ -31,7 +31,7 @@ namespace dq4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDwordsPerLane = 4;
+constexpr int kDwordsPerLane = 2;
 constexpr int kTileDwords = kThreads * kDwordsPerLane;
 constexpr int kTileElems = kTileDwords * 8;
 constexpr int kMaxTileBlocks = kTileElems / 32 + 1;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         }
         using Word = typename Unit<OUT>::Word;
         constexpr int E = Unit<OUT>::kElems;
-        constexpr int kUnits = 32 / E;  // units per lane and tile
+        constexpr int kUnits = kDwordsPerLane * 8 / E;  // units per lane and tile
         const Word *wp = reinterpret_cast<const Word *>(packed);
         const int64_t u0 = d0 * 8 / E;
         Word w[kUnits];

@@ -71,7 +71,7 @@ def test_every_scale_code_and_4bit_code(fmt, dt, blocksize):
 @pytest.mark.parametrize("blocksize", inputs.TAIL_SWEEP_BLOCKSIZES)
 def test_tails_partial_blocks_and_groups(blocksize):
     B = blocksize
-    lengths = [1, 2, 3, 7, 8, 9, B - 1, B, B + 1, 8191, 8192, 8193, 16383, 16384, 16385,
+    lengths = [1, 2, 3, 7, 8, 9, B - 1, B, B + 1, 4095, 4096, 4097, 8191, 8192, 8193, 16385,
                32769, 256 * B - 1, 256 * B,
                256 * B + 1, 256 * B + B + 1, 2 * 256 * B + 3 * B + 17]
     for n in lengths:
@@ -84,7 +84,7 @@ def test_tails_partial_blocks_and_groups(blocksize):
 def test_output_is_not_written_past_n():
     """Canaries after `out`: elements past n keep their values, on the vector
     path (aligned) and the per-element path (misaligned), for every dtype."""
-    for n in (1, 13, 8191, 8192 + 5, 16384 + 5, 3 * 16384 + 1):
+    for n in (1, 13, 4095, 4096 + 5, 8192 + 5, 3 * 4096 + 1):
         for dt in ("f32", "f16", "bf16"):
             x = inputs.make_inputs(n, 32, "nf4", 0.03, seed=n)
             dev = dq4.to_device(x)
