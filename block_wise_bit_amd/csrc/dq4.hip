@@ -21,17 +21,23 @@
 //    bytes for every output type.  One tile per workgroup, in dispatch order,
 //    keeps the set of addresses being written compact; on MI355X this writes
 //    markedly faster than a persistent grid-stride loop, and 4096-element
-//    tiles measured ~4 % faster than 8192 and 2 % faster than 6144;
-//  * the packed loads are issued first; while they are in flight the
-//    workgroup rebuilds the scale of each outer block its tile touches (at
+//    tiles measured faster than 2048 (by ~45 %), 6144 (~0.3 %) and 8192
+//    (~10 %) elements;
+//  * the packed loads are issued first (non-temporal for FP16/BF16 output:
+//    each byte is read once); while they are in flight the workgroup rebuilds the scale of each outer block its tile touches (at
 //    most 129), one block per lane, into LDS -- so the scale is computed once
 //    per block, never stored to HBM, and the value pass reads it from LDS;
 //  * the 256-entry scale codebook and the 16-entry value codebook sit in LDS;
 //    the 16-entry table covers 16 distinct banks, so lookups never conflict;
 //  * since blocksize >= 32 and the window starts on a multiple of 8, the
 //    elements of a unit share one outer block;
-//  * outputs are written with non-temporal stores (streamed, not kept in
-//    cache);
+//  * outputs are written with 16-byte buffer stores marked nt and sc1
+//    (streamed at device scope; ~3 % faster than nt alone on MI355X);
+//  * with blocksize >= 64, neighbouring tiles read the same 128-byte line of
+//    scale codes; for FP16/BF16 output the slot -> tile map puts such tiles
+//    on one XCD so that the line is fetched from HBM once (workgroups go to
+//    the 8 XCDs in turn, and each XCD has its own L2).  FP32 output measured
+//    faster with plain loads in dispatch order (kStreamPolicy);
 //  * the partial last tile, and any window that does not meet the alignment
 //    of the vector path, go through a per-element path that computes the same
 //    bits.
@@ -57,6 +63,8 @@ constexpr int kTileDwords = kThreads * kDwordsPerLane;
 constexpr int kTileElems = kTileDwords * 8;    // 4096
 constexpr int kMaxTileBlocks = kTileElems / 32 + 1;  // blocksize 32, tile not block-aligned
 constexpr int kElemBlocksPerCU = 8;            // grid of the per-element path
+constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kLog2MaxShare = 3;  // pair up at most 8 tiles per line of scale codes
 
 struct Args {
     const uint8_t *packed;
@@ -98,6 +106,18 @@ __device__ __forceinline__ void one_element(const Args &a, const float *lds_scb,
     store1<OUT>(a.out, j, lds_cb4[k] * s);
 }
 
+// Workgroups are dispatched to the XCDs in turn (workgroup i to XCD i mod 8),
+// and each XCD has its own L2.  With blocksize 2^lb, 2^(lb-5) consecutive
+// tiles read the same 128-byte line of scale codes; this bijection of each
+// aligned group of 8 * 2^s slots gives those 2^s tiles slots that are 8
+// apart, hence one XCD, so the line is fetched from HBM once, not 2^s times.
+__device__ __forceinline__ int64_t xcd_paired_tile(int64_t slot, int s)
+{
+    const int64_t group = slot & ~((int64_t{kXcds} << s) - 1);
+    const int64_t x = slot - group;
+    return group | ((x % kXcds) << s) | (x / kXcds);
+}
+
 // Vector path.  Requires e0 % 8 == 0, packed + e0/2 4-byte aligned and out
 // 16-byte aligned.  Tiles [0, n_full) are full; tile n_full (if any) is the
 // partial last tile.  Normally gridDim.x == n_tiles and each workgroup runs
@@ -113,7 +133,13 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
     const int t = threadIdx.x;
     const int lb = a.log2_block;
 
-    for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // FP16/BF16: tiles that read the same 128-byte line of scale codes run on
+    // one XCD (FP32 keeps dispatch order; see kStreamPolicy)
+    const int log2_share = min(lb - 5, kLog2MaxShare);  // tiles per line of codes
+    const int64_t n_paired =
+        kStreamPolicy<OUT> ? n_full & ~((int64_t{kXcds} << log2_share) - 1) : 0;
+    for (int64_t slot = blockIdx.x; slot < n_tiles; slot += gridDim.x) {
+        const int64_t tile = slot < n_paired ? xcd_paired_tile(slot, log2_share) : slot;
         const int64_t d0 = tile * kTileDwords;  // first packed dword of the tile
         if (tile >= n_full) {
             load_tables(a, lds_scb, lds_cb4);
@@ -132,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         Word w[kUnits];
 #pragma unroll
         for (int u = 0; u < kUnits; ++u)
-            w[u] = words[u0 + u * kThreads + t];
+            w[u] = load_packed<OUT>(words + u0 + u * kThreads + t);
 
         // 2. metadata of the outer blocks this tile touches, one block per lane
         const int64_t e_tile = a.e0 + d0 * 8;
@@ -161,6 +187,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         __syncthreads();
 
         // 4. value pass: E elements per unit, one 16-byte store per unit
+        const __amdgpu_buffer_rsrc_t dst = unit_buffer(a.out, u0, kUnits * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const uint32_t ul = u * kThreads + t;
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[e] = lds_cb4[(static_cast<uint32_t>(w[u]) >> (4 * e)) & 0xFu] * s;
-            store_unit<OUT>(a.out, u0 + ul, v);
+            store_unit<OUT>(dst, ul, v);
         }
         __syncthreads();  // LDS is rewritten by the next tile of this workgroup
     }

@@ -76,27 +76,63 @@ struct Unit {
     using Word = typename std::conditional<OUT == DQ4_F32, uint16_t, uint32_t>::type;
 };
 
-// The decoded FP32 values of unit u, written as output type OUT with a
-// streaming 16-byte store (unit u covers elements [u * kElems, ...)).
+// Memory policy of the vector paths, by output type (measured on MI355X with
+// cold inputs).  With FP16/BF16 output (4 B written per 1 B read) the packed
+// loads are non-temporal and tiles sharing a line of scale codes are placed
+// on one XCD; each was worth ~0.5 % at 28672 x 8192.  With FP32 output (8 B
+// written per 1 B read) both made the kernel slower -- ~13 % together at
+// 28672 x 8192 -- so that instantiation uses plain loads in dispatch order.
 template <int OUT>
-__device__ __forceinline__ void store_unit(void *out, int64_t u,
-                                           const float (&v)[Unit<OUT>::kElems])
+constexpr bool kStreamPolicy = OUT != DQ4_F32;
+
+template <int OUT, typename Word>
+__device__ __forceinline__ Word load_packed(const Word *p)
 {
-    if constexpr (OUT == DQ4_F32) {
-        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]},
-                                    reinterpret_cast<f32x4 *>(out) + u);
-    } else if constexpr (OUT == DQ4_F16) {
-        __builtin_nontemporal_store(u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
-                                          pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])},
-                                    reinterpret_cast<u32x4 *>(out) + u);
-    } else {
-        __builtin_nontemporal_store(u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
-                                    reinterpret_cast<u32x4 *>(out) + u);
-    }
+    if constexpr (kStreamPolicy<OUT>)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
 }
 
-// One FP32 value written as output type OUT at element index j.
+// Output stores of the vector paths go through a raw buffer resource that
+// covers the units of one tile, with two cache-policy bits set: nt (streamed,
+// not kept for reuse) and sc1 (device scope).  On MI355X, 16-byte stores with
+// nt and sc1 measured ~3 % faster over a whole dequantization than stores with
+// nt alone, and sc1 without nt was slower than both.  A raw buffer store also
+// drops any access past the resource's byte range instead of writing there.
+//
+// Dword 3 of the resource: 32-bit data format (bits 18:15 = 4), no index
+// stride, no swizzle -- the plain untyped-buffer layout of the gfx9 family.
+constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy immediate of a gfx950 vector memory instruction.
+constexpr int kPolicyNT = 2;    // non-temporal
+constexpr int kPolicySC1 = 16;  // scope bit 1 (device scope)
+
+// The buffer for n_units 16-byte units of `out` starting at unit u0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_buffer(void *out, int64_t u0,
+                                                              uint32_t n_units)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(out) + u0 * 16, 0,
+                                             n_units * 16, kRawBufferWord3);
+}
+
+// The decoded FP32 values of one unit, written as output type OUT with one
+// 16-byte store at unit `ul` of the buffer.
+template <int OUT>
+__device__ __forceinline__ void store_unit(__amdgpu_buffer_rsrc_t dst, uint32_t ul,
+                                           const float (&v)[Unit<OUT>::kElems])
+{
+    u32x4 q;
+    if constexpr (OUT == DQ4_F32)
+        q = __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]});
+    else if constexpr (OUT == DQ4_F16)
+        q = u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                  pack_f16x2(v[6], v[7])};
+    else
+        q = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(q, dst, ul * 16, 0, kPolicyNT | kPolicySC1);
+}
 template <int OUT>
 __device__ __forceinline__ void store1(void *out, int64_t j, float v)
 {

@@ -15,8 +15,11 @@
 // per block) and two extra launches -- the cost the fusion removes.
 //
 // Launch 3 has the same tile structure as the fused kernel (256 lanes, 4096
-// elements per workgroup, streaming stores), so the comparison measures the
-// fusion and nothing else.
+// elements per workgroup, the same load policy per output type, the same
+// nt + sc1 output stores), so the comparison measures the fusion and nothing
+// else.  (The fused kernel also places tiles that share a line of scale
+// codes on one XCD; here each tile reads its own lines of the FP32 buffer,
+// so there is nothing to pair.)
 
 #include <hip/hip_runtime.h>
 
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         Word w[kUnits];
 #pragma unroll
         for (int u = 0; u < kUnits; ++u)
-            w[u] = wp[u0 + u * kThreads + t];
+            w[u] = load_packed<OUT>(wp + u0 + u * kThreads + t);
         const int64_t b0 = (d0 * 8) >> log2_block;
         const uint32_t r = static_cast<uint32_t>(d0 * 8 - (b0 << log2_block));
         const int n_blocks = static_cast<int>((r + kTileElems - 1) >> log2_block) + 1;
@@ -101,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         if (t < 16)
             lds_cb4[t] = cv;
         __syncthreads();
+        const __amdgpu_buffer_rsrc_t dst = unit_buffer(out, u0, kUnits * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const uint32_t ul = u * kThreads + t;
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[e] = lds_cb4[(static_cast<uint32_t>(w[u]) >> (4 * e)) & 0xFu] * s;
-            store_unit<OUT>(out, u0 + ul, v);
+            store_unit<OUT>(dst, ul, v);
         }
     }
 }

@@ -86,3 +86,27 @@ def test_no_scratch(asm):
     """The scale lives in registers: no private (scratch) segment is used."""
     vals = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", asm)
     assert vals and all(v == "0" for v in vals)
+
+
+def test_tile_kernels_stream_their_memory_traffic(asm):
+    """The vector paths write every output unit with a 16-byte buffer store
+    marked nt and sc1 (the measured-fastest store policy on MI355X), and no
+    other kind of 16-byte store appears in them.  The packed data is read
+    with non-temporal loads for FP16/BF16 output (instantiations 1 and 2) and
+    with plain loads for FP32 output (instantiation 0), as measured fastest."""
+    for name, code in _kernel_bodies(asm).items():
+        if "dq4_tile_kernel" not in name and "dq4_value_tile_kernel" not in name:
+            continue
+        stores = re.findall(r"^\s*(buffer_store_dwordx4|global_store_dwordx4)\b(.*)$", code,
+                            re.M)
+        assert stores, name
+        for op, operands in stores:
+            assert op == "buffer_store_dwordx4", (name, op)
+            flags = set(operands.split())
+            assert {"nt", "sc1"} <= flags and "sc0" not in flags, (name, operands)
+        packed = re.findall(r"^\s*global_load_(?:dword|ushort)\b(.*)$", code, re.M)
+        assert packed, name
+        if "ILi0E" in name:
+            assert not any(" nt" in p for p in packed), name
+        else:
+            assert any(" nt" in p for p in packed), name
