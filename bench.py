@@ -240,11 +240,14 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
 
 
 def out_prod_bench(args, torch, dq4, inputs) -> int:
-    """Row-blocked out_prod of the 151936 x 5376 NF4 output head against a
-    src1 of m rows per weight row (the LoRA backward of the output head in
-    the llama.cpp PR): 13 F32 windows of <= 256 MiB, one FP32 GEMM each.
-    Reports the whole call, the dequantization share (the windows alone),
-    and the single-window whole-copy variant for comparison."""
+    """out_prod of the 151936 x 5376 NF4 output head against a src1 of m
+    rows per weight row (the LoRA backward of the output head in the
+    llama.cpp PR), by both routes:
+    * row-blocked: 13 F32 windows of <= 256 MiB, one FP32 library GEMM each
+      (also timed: the windows' dequantization alone, and the single-window
+      whole copy);
+    * fused: the weight decoded inside an FP32 matrix-core GEMM, no window.
+    The two results must agree within twice the FP32 summation bound."""
     wl = inputs.OUTPUT_HEAD
     x = wl.inputs()
     dev = dq4.to_device(x, "cuda:0")
@@ -257,6 +260,10 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
     ws = torch.empty(rows_pb * wl.n_cols, dtype=torch.float32, device="cuda:0")
     windows = dq4.dq4_row_windows(wl.n_rows, wl.n_cols, 4, budget)
     flops = 2.0 * m * wl.n_rows * wl.n_cols
+    fused_ws_bytes = dq4.dq4_out_prod_fused_workspace_bytes(wl.n_rows, wl.n_cols, m)
+    fused_ws = torch.empty(max(fused_ws_bytes // 4, 0), dtype=torch.float32, device="cuda:0")
+    kw = dict(offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols, blocksize=64,
+              src1=src1)
 
     def timeit(fn, reps):
         for _ in range(2):
@@ -271,8 +278,10 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
         return a.elapsed_time(b) / reps  # ms
 
     def blocked():
-        dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols,
-                              blocksize=64, src1=src1, dst=dst, workspace=ws)
+        dq4.dq4_out_prod_rows(**dev, **kw, dst=dst, workspace=ws)
+
+    def fused():
+        dq4.dq4_out_prod_fused(**dev, **kw, dst=dst, workspace=fused_ws)
 
     def windows_only():
         for r0, rows in windows:
@@ -282,29 +291,40 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
 
     reps = max(3, args.steps // 100)
     t_blocked = timeit(blocked, reps)
-    t_dequant = timeit(windows_only, reps)
     out_blocked = dst.clone()
+    t_fused = timeit(fused, reps)
+    out_fused = dst.clone()
+    t_dequant = timeit(windows_only, reps)
     whole = torch.empty(wl.n_rows * wl.n_cols, dtype=torch.float32, device="cuda:0")
 
     def whole_copy():
-        dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols,
-                              blocksize=64, src1=src1, dst=dst, workspace=whole)
+        dq4.dq4_out_prod_rows(**dev, **kw, dst=dst, workspace=whole)
 
     t_whole = timeit(whole_copy, reps)
-    rel = float((dst - out_blocked).abs().max() / out_blocked.abs().max().clamp_min(1e-30))
+    del whole
+    scale = out_blocked.abs().max().clamp_min(1e-30)
+    rel_whole = float((dst - out_blocked).abs().max() / scale)
+    rel_fused = float((out_fused - out_blocked).abs().max() / scale)
+    tflops = {name: round(flops / (t * 1e-3) / 1e12, 2)
+              for name, t in (("fused", t_fused), ("blocked", t_blocked), ("whole", t_whole))}
+    best = max(tflops.values())
     print(json.dumps({
-        "metric": "row-blocked out_prod of the 151936x5376 NF4 output head, FP32 GEMM TFLOP/s",
-        "value": round(flops / (t_blocked * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-        "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+        "metric": "out_prod of the 151936x5376 NF4 output head, FP32 TFLOP/s (fused route)",
+        "value": tflops["fused"], "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
+        "data": "synthetic",
         "config": {"workload": wl.name, "m": m, "windows": len(windows),
-                   "rows_per_window": rows_pb, "transient_bytes": rows_pb * wl.n_cols * 4},
-        "ms_blocked": round(t_blocked, 4), "ms_dequant_windows": round(t_dequant, 4),
-        "dequant_share": round(t_dequant / t_blocked, 4),
-        "ms_whole_copy": round(t_whole, 4), "whole_copy_transient_bytes": whole.numel() * 4,
-        "blocked_vs_whole_max_rel_diff": rel,
-        "roofline": {"bound": "mfma", "achieved": round(flops / (t_blocked * 1e-3) / 1e12, 2),
-                     "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(flops / (t_blocked * 1e-3) / 1e12 / 157.3, 4)},
+                   "rows_per_window": rows_pb, "transient_bytes": rows_pb * wl.n_cols * 4,
+                   "fused_workspace_bytes": fused_ws_bytes},
+        "ms_fused": round(t_fused, 4), "ms_blocked": round(t_blocked, 4),
+        "ms_dequant_windows": round(t_dequant, 4),
+        "dequant_share_of_blocked": round(t_dequant / t_blocked, 4),
+        "ms_whole_copy": round(t_whole, 4), "whole_copy_transient_bytes":
+            wl.n_rows * wl.n_cols * 4,
+        "TFLOPs": tflops, "fused_speedup_vs_blocked": round(t_blocked / t_fused, 3),
+        "blocked_vs_whole_max_rel_diff": rel_whole, "fused_vs_blocked_max_rel_diff": rel_fused,
+        "roofline": {"bound": "mfma", "achieved": tflops["fused"], "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(tflops["fused"] / 157.3, 4)},
+        "best_route_TFLOPs": best,
         "device": torch.cuda.get_device_name(0)}), flush=True)
     return 0
 
@@ -601,28 +621,63 @@ def main() -> int:
     }
 
     if not args.no_cpu:
+        import concurrent.futures
+
         import oracle
 
         got = sets[(K - 1) % len(sets)][1].cpu().view(torch.int16).numpy().view(np.uint16)
-        passes, t_cpu, want = 0, 0.0, None
-        while passes < 3 and (passes == 0 or t_cpu < args.cpu_seconds):
-            c0 = time.perf_counter()
-            want = oracle.dequant(x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook,
-                                  x.codebook4, x.offset, n, bs, out_dtype="f16")
-            t_cpu += time.perf_counter() - c0
-            passes += 1
-            print(f"[bench] oracle pass {passes}: {t_cpu:.2f} s so far", file=sys.stderr,
-                  flush=True)
+
+        def oracle_pass(threads):
+            """One oracle pass over the whole tensor, split into `threads`
+            disjoint element ranges run concurrently (the C oracle releases
+            the GIL while it runs)."""
+            want = np.empty(n, dtype=np.uint16)
+            chunk = -(-n // threads)
+            chunk += (-chunk) % 8
+
+            def one(start):
+                c = min(chunk, n - start)
+                want[start:start + c] = oracle.dequant_range(
+                    x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook, x.codebook4,
+                    x.offset, start, c, bs, x.nested_blocksize, "f16")
+
+            with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+                list(pool.map(one, range(0, n, chunk)))
+            return want
+
+        def timed_passes(threads):
+            passes, t_cpu, want = 0, 0.0, None
+            while passes < 3 and (passes == 0 or t_cpu < args.cpu_seconds):
+                c0 = time.perf_counter()
+                want = oracle_pass(threads)
+                t_cpu += time.perf_counter() - c0
+                passes += 1
+                print(f"[bench] oracle on {threads} thread(s), pass {passes}: {t_cpu:.2f} s so "
+                      f"far", file=sys.stderr, flush=True)
+            return passes, t_cpu, want
+
+        # the box's CPU share, whatever os.cpu_count() reports there
+        threads = max(1, min(16, os.cpu_count() or 1))
+        passes, t_cpu, want = timed_passes(threads)
+        passes1, t_cpu1, want1 = timed_passes(1)
         mismatches = int(np.count_nonzero(got != want))
-        cpu_gbs = alg_bytes * passes / t_cpu / 1e9
+        host = (f"host {platform.processor() or platform.machine()} with {os.cpu_count()} "
+                f"logical cpus")
         result["cpu_baseline"] = {
-            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {wl.n_rows}x{wl.n_cols} tensor, {passes} single-threaded "
-                      f"pass(es), {t_cpu:.2f} s; host {platform.processor() or platform.machine()}"
-                      f" with {os.cpu_count()} logical cpus",
-            "elements_per_s": round(n * passes / t_cpu, 1)}
+            "value": round(alg_bytes * passes / t_cpu / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"whole {wl.n_rows}x{wl.n_cols} tensor, {passes} pass(es) on {threads} "
+                      f"threads over disjoint element ranges, {t_cpu:.2f} s; {host}",
+            "elements_per_s": round(n * passes / t_cpu, 1),
+            "single_core": {"value": round(alg_bytes * passes1 / t_cpu1 / 1e9, 4),
+                            "unit": "GB/s", "cores": 1,
+                            "sample": f"whole tensor, {passes1} single-threaded pass(es), "
+                                      f"{t_cpu1:.2f} s",
+                            "elements_per_s": round(n * passes1 / t_cpu1, 1)}}
         result["parity"] = {"compared_elements": n, "mismatches": mismatches,
-                            "bit_exact": mismatches == 0}
+                            "bit_exact": mismatches == 0,
+                            "threaded_oracle_equals_single_threaded":
+                                bool(np.array_equal(want, want1))}
 
     print(json.dumps(result), flush=True)
     if result["parity"] is not None and not result["parity"]["bit_exact"]:

@@ -16,6 +16,9 @@ cannot be loaded, every call raises.
     dq4_unfused_workspace_bytes(n, blocksize) -> int
     dq4_out_prod_rows(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
                                                    (row-blocked out_prod, FP32 GEMM)
+    dq4_out_prod_fused(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
+                                                   (out_prod, dequantization in the GEMM)
+    dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m) -> int
     dq4_dequant_linear(..., n_out, n_in, blocksize, x, op) -> tensor
                                                    (Y = X W^T or G W, FP16/BF16 GEMM)
     dq4_int8_prep(A, CB, SCB, cols) -> (subA, subB)  (LLM.int8 correction operands)
@@ -70,6 +73,10 @@ def library() -> ctypes.CDLL:
     lib.dq4_out_prod_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, P, i64, i64, i32, P,
                                       P, i64, P]
     lib.dq4_out_prod_rows.restype = i32
+    lib.dq4_out_prod_fused.argtypes = lib.dq4_out_prod_rows.argtypes
+    lib.dq4_out_prod_fused.restype = i32
+    lib.dq4_out_prod_fused_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dq4_out_prod_fused_workspace_bytes.restype = i64
     lib.dq4_dequant_linear.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, i32, i32, P, i64,
                                        P, P, P]
     lib.dq4_dequant_linear.restype = i32
@@ -280,22 +287,9 @@ def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codeboo
     return out
 
 
-def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
-                      offset: float, n_rows: int, n_cols: int, blocksize: int, src1,
-                      src1_transposed: bool = False, dst=None, workspace=None,
-                      workspace_bytes: int = ROW_BLOCK_BUDGET_BYTES,
-                      nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
-    """dst[i][j] = sum_r B[r][i] * W[r][j] for the nested 4-bit weight W
-    (n_rows x n_cols), dequantized to FP32 in row windows of at most
-    `workspace_bytes` and accumulated by an FP32 GEMM per window.
-
-    src1 is FP32, 2-D with unit stride along its last dimension: shape
-    (n_rows, m) (B = src1) or, with src1_transposed, (m, n_rows) (B = src1^T).
-    Returns dst (m x n_cols, FP32).  `workspace` (FP32, at least one row of
-    n_cols) is allocated when None, sized min(workspace_bytes, whole weight).
-    """
-    torch = _torch()
-    n_rows, n_cols = int(n_rows), int(n_cols)
+def _out_prod_operands(torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                       n_rows, n_cols, blocksize, nested_blocksize, src1, src1_transposed, dst):
+    """Checked (device, m, ld, dst) for the two out_prod entry points."""
     device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
                            n_rows * n_cols, int(blocksize), int(nested_blocksize))
     if src1.device != device or src1.dtype != torch.float32 or src1.dim() != 2:
@@ -312,12 +306,39 @@ def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebo
     elif (dst.device != device or dst.dtype != torch.float32 or not dst.is_contiguous()
           or dst.numel() < m * n_cols):
         raise ValueError("dst must be a contiguous float32 tensor of m * n_cols values")
+    return device, m, ld, dst
+
+
+def _f32_workspace(torch, workspace, device):
+    if (workspace.device != device or workspace.dtype != torch.float32
+            or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 tensor on the inputs' device")
+    return workspace
+
+
+def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                      offset: float, n_rows: int, n_cols: int, blocksize: int, src1,
+                      src1_transposed: bool = False, dst=None, workspace=None,
+                      workspace_bytes: int = ROW_BLOCK_BUDGET_BYTES,
+                      nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
+    """dst[i][j] = sum_r B[r][i] * W[r][j] for the nested 4-bit weight W
+    (n_rows x n_cols), dequantized to FP32 in row windows of at most
+    `workspace_bytes` and accumulated by an FP32 GEMM per window.
+
+    src1 is FP32, 2-D with unit stride along its last dimension: shape
+    (n_rows, m) (B = src1) or, with src1_transposed, (m, n_rows) (B = src1^T).
+    Returns dst (m x n_cols, FP32).  `workspace` (FP32, at least one row of
+    n_cols) is allocated when None, sized min(workspace_bytes, whole weight).
+    """
+    torch = _torch()
+    n_rows, n_cols = int(n_rows), int(n_cols)
+    device, m, ld, dst = _out_prod_operands(
+        torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4, n_rows, n_cols,
+        blocksize, nested_blocksize, src1, src1_transposed, dst)
     if workspace is None:
         rows = max(1, min(n_rows, int(workspace_bytes) // max(4 * n_cols, 1)))
         workspace = torch.empty(max(rows * n_cols, 1), dtype=torch.float32, device=device)
-    elif (workspace.device != device or workspace.dtype != torch.float32
-          or not workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous float32 tensor on the inputs' device")
+    workspace = _f32_workspace(torch, workspace, device)
     with torch.cuda.device(device):
         st = library().dq4_out_prod_rows(
             packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
@@ -326,6 +347,44 @@ def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebo
             1 if src1_transposed else 0, dst.data_ptr(), workspace.data_ptr(),
             workspace.numel() * 4, _stream_handle(device, stream))
     _raise_for(st, "dq4_out_prod_rows")
+    return dst
+
+
+def dq4_out_prod_fused_workspace_bytes(n_rows: int, n_cols: int, m: int, device=None) -> int:
+    """Workspace bytes for dq4_out_prod_fused's preferred row split on
+    `device` (default: the current device); 0 when it prefers one split."""
+    torch = _torch()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(library().dq4_out_prod_fused_workspace_bytes(int(n_rows), int(n_cols),
+                                                                int(m)))
+
+
+def dq4_out_prod_fused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                       offset: float, n_rows: int, n_cols: int, blocksize: int, src1,
+                       src1_transposed: bool = False, dst=None, workspace=None,
+                       nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
+    """The same sum as dq4_out_prod_rows, with the 4-bit weight decoded inside
+    an FP32 matrix-core GEMM (no dequantized copy in HBM).  `workspace`
+    (FP32, for partial sums over row splits) is allocated at the preferred
+    size when None; an empty tensor means one split.  Returns dst."""
+    torch = _torch()
+    n_rows, n_cols = int(n_rows), int(n_cols)
+    device, m, ld, dst = _out_prod_operands(
+        torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4, n_rows, n_cols,
+        blocksize, nested_blocksize, src1, src1_transposed, dst)
+    if workspace is None:
+        nbytes = dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, device)
+        workspace = torch.empty(max(nbytes // 4, 0), dtype=torch.float32, device=device)
+    workspace = _f32_workspace(torch, workspace, device)
+    with torch.cuda.device(device):
+        st = library().dq4_out_prod_fused(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), n_rows,
+            n_cols, int(blocksize), int(nested_blocksize), src1.data_ptr(), m, ld,
+            1 if src1_transposed else 0, dst.data_ptr(),
+            workspace.data_ptr() if workspace.numel() else None, workspace.numel() * 4,
+            _stream_handle(device, stream))
+    _raise_for(st, "dq4_out_prod_fused")
     return dst
 
 

@@ -20,7 +20,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", name)
-           for name in ("dq4.hip", "dq4_unfused.hip", "dq4_gemm.hip", "dq4_int8_prep.hip")]
+           for name in ("dq4.hip", "dq4_unfused.hip", "dq4_gemm.hip", "dq4_out_prod_fused.hip",
+                        "dq4_int8_prep.hip")]
 LIBS = ["-lrocblas"]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libdq4.so")

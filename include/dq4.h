@@ -183,6 +183,50 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
                                int64_t workspace_bytes, void *stream);
 
 /*
+ * out_prod with the dequantization fused into the GEMM (llama.cpp PR "cuda:
+ * out_prod dequantizes a 2D weight in row blocks": the approving review names
+ * the fused dequant-in-GEMM route as the follow-on of the row-blocked path).
+ * Same sum, same arguments and same layouts as dq4_out_prod_rows:
+ *
+ *     dst[i][j] = sum over r in [0, n_rows) of B[r][i] * W[r][j]
+ *
+ * but no dequantized copy of W is written: each workgroup decodes its part
+ * of the 4-bit weight into on-chip memory as exactly the FP32 values
+ * dq4_nested_dequant writes, and multiplies on the matrix cores in FP32.
+ * The summation order differs from dq4_out_prod_rows; both are within the
+ * FP32 summation bound of the exact sum.
+ *
+ * workspace: optional caller-owned device memory for partial sums.  When the
+ * dst tiles alone cannot fill the GPU, the rows are split and each split's
+ * partial dst (m * n_cols FP32) goes to the workspace, then one more kernel
+ * adds the partials in split order into dst.  The number of splits is the
+ * largest of those the workspace holds up to the preferred count
+ * (dq4_out_prod_fused_workspace_bytes); with workspace_bytes == 0 there is
+ * one split and dst is written directly.  The workspace changes speed only;
+ * the result is deterministic for a given device and workspace size.
+ *
+ * dst is overwritten (n_rows == 0 writes zeros); m == 0 or n_cols == 0 is a
+ * no-op.  Everything is enqueued on `stream`; nothing is allocated or
+ * synchronized.  Errors: DQ4_EINVAL for bad sizes, a leading dimension that
+ * is too small, a null pointer, or workspace_bytes > 0 with a null
+ * workspace; DQ4_EUNSUPPORTED for a tile grid of more than 2^31 - 1
+ * workgroups; layout errors as for dq4_nested_dequant.
+ */
+dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_codes,
+                                const float *nested_absmax, const float *scale_codebook,
+                                const float *codebook4, float offset, int64_t n_rows,
+                                int64_t n_cols, int32_t blocksize, int32_t nested_blocksize,
+                                const float *src1, int64_t m, int64_t ld_src1,
+                                int32_t src1_transposed, float *dst, float *workspace,
+                                int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes at which dq4_out_prod_fused uses its preferred number of
+ * row splits on the current device (0 when one split is preferred, or for
+ * non-positive or oversized arguments).  Host only; queries the current
+ * device. */
+int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m);
+
+/*
  * Dequantize-plus-linear (bitsandbytes issue above, section "Problem": the
  * dequantize-plus-linear fallback that materializes the full weight before
  * F.linear, and MatMul4Bit.backward's grad_A, which uses the same

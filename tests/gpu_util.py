@@ -1,7 +1,8 @@
 """Helpers for the GPU parity tests: run the HIP path and the oracle on the
 same host inputs and hand back raw output bits.  No arithmetic of the method
 lives here -- the oracle computes, these functions only split ranges across
-threads and move buffers."""
+threads and move buffers (and, for the out_prod tests, sum the oracle's
+weight against src1 in float64 with numpy)."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -68,3 +69,35 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
 def say(*args):
     print(*args, flush=True)
     sys.stdout.flush()
+
+
+U32 = 2.0 ** -24   # unit roundoff of binary32
+
+
+def out_prod_reference(x, n_rows, n_cols, b_rows_by_m, chunk_rows=16384):
+    """float64 sum_r B[r][i] W[r][j] and sum_r |B[r][i]| |W[r][j]|, with W the
+    oracle's F32 dequantization of the n_rows x n_cols weight x."""
+    m = b_rows_by_m.shape[1]
+    exact = np.zeros((m, n_cols))
+    mag = np.zeros((m, n_cols))
+    for r0 in range(0, n_rows, chunk_rows):
+        rows = min(chunk_rows, n_rows - r0)
+        w = oracle_bits(x, "f32", r0 * n_cols, rows * n_cols).view(np.float32)
+        w = w.reshape(rows, n_cols).astype(np.float64)
+        b = b_rows_by_m[r0:r0 + rows].astype(np.float64)
+        exact += b.T @ w
+        mag += np.abs(b).T @ np.abs(w)
+    return exact, mag
+
+
+def check_sum_bound(got, exact, mag, K, what, factor=1.0):
+    """Every element within factor * gamma_K * mag of the exact sum, where
+    gamma_K = K u / (1 - K u): the bound of any FP32 summation of K products,
+    in any order and with or without fused multiply-adds."""
+    gamma = K * U32 / (1 - K * U32)
+    err = np.abs(got.astype(np.float64) - exact)
+    bound = factor * gamma * mag
+    worst = np.max(err / np.maximum(bound, 1e-300))
+    say(f"{what}: max |err| {err.max():.3e}, worst err/bound {worst:.3e}")
+    assert np.isfinite(got).all(), what
+    assert (err <= bound).all(), f"{what}: error above the FP32 summation bound"

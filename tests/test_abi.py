@@ -27,7 +27,8 @@ def test_exports_every_declared_function(lib):
                           "dq4_status_string", "dq4_last_hip_error",
                           "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
                           "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear",
-                          "dq4_int8_prep"}
+                          "dq4_int8_prep", "dq4_out_prod_fused",
+                          "dq4_out_prod_fused_workspace_bytes"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -103,6 +104,32 @@ def test_validation_out_prod(lib):
     assert call(dst=None) == dq4.DQ4_EINVAL
     assert call(m=1 << 31, ld=1 << 31) == dq4.DQ4_EINVAL   # beyond the 32-bit GEMM interface
     assert call(blocksize=7) == dq4.DQ4_EUNSUPPORTED
+
+
+def test_validation_out_prod_fused(lib):
+    p = ctypes.c_void_p(1)
+
+    def call(n_rows=100, n_cols=64, m=8, ld=8, trans=0, ws_bytes=0, blocksize=64, ws=None,
+             src=p, dst=p, nested=256):
+        return lib.dq4_out_prod_fused(p, p, p, p, p, ctypes.c_float(0.0), n_rows, n_cols,
+                                      blocksize, nested, src, m, ld, trans, dst, ws, ws_bytes,
+                                      None)
+    assert call(m=0) == dq4.DQ4_OK                    # empty dst: nothing to do
+    assert call(n_cols=0) == dq4.DQ4_OK
+    assert call(n_rows=-1) == dq4.DQ4_EINVAL
+    assert call(m=-1) == dq4.DQ4_EINVAL
+    assert call(trans=2) == dq4.DQ4_EINVAL
+    assert call(ld=7) == dq4.DQ4_EINVAL               # ld < m
+    assert call(trans=1, ld=99) == dq4.DQ4_EINVAL     # ld < n_rows
+    assert call(ws_bytes=-4) == dq4.DQ4_EINVAL
+    assert call(ws_bytes=1024, ws=None) == dq4.DQ4_EINVAL   # a size without a buffer
+    assert call(src=None) == dq4.DQ4_EINVAL
+    assert call(dst=None) == dq4.DQ4_EINVAL
+    assert call(blocksize=7) == dq4.DQ4_EUNSUPPORTED
+    assert call(nested=128) == dq4.DQ4_EUNSUPPORTED
+    assert call(m=(1 << 31) * 64, ld=(1 << 31) * 64) == dq4.DQ4_EUNSUPPORTED  # > 2^31 - 1 tiles
+    for args in ((0, 64, 8), (100, 0, 8), (100, 64, 0), (-1, 64, 8), (1 << 40, 1 << 40, 1 << 40)):
+        assert lib.dq4_out_prod_fused_workspace_bytes(*args) == 0
 
 
 def test_validation_linear(lib):

@@ -42,7 +42,9 @@ def test_kernels_present(asm):
     for kernel, count in (("dq4_tile_kernel", 3), ("dq4_elem_kernel", 3),
                           ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
-                          ("zero_fill_kernel", 1), ("int8_prep_kernel", 1)):
+                          ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
+                          ("out_prod_fused_kernel", 2), ("out_prod_reduce_kernel", 1),
+                          ("out_prod_zero_kernel", 1)):
         assert sum(kernel in n for n in names) == count, kernel
 
 
@@ -50,12 +52,14 @@ def test_no_fused_or_packed_fp_instructions(asm):
     for name, code in _kernel_bodies(asm).items():
         found = sorted(set(FORBIDDEN.findall(code)))
         assert not found, f"{name}: {found}"
-        if "add_offset" in name:
+        if "add_offset" in name or "reduce" in name:
             assert "v_add_f32" in code, name
-        elif "zero_fill" not in name:
+        elif "zero_fill" not in name and "zero_kernel" not in name:
             assert "v_mul_f32" in code, name
-        if "dq4_tile_kernel" in name or "dq4_elem_kernel" in name:
+        if "dq4_tile_kernel" in name or "dq4_elem_kernel" in name or "out_prod_fused" in name:
             assert "v_add_f32" in code, name   # the scale is rebuilt in the fused kernels
+        if "out_prod_fused" in name:           # FP32 matrix cores, and only those
+            assert set(re.findall(r"\bv_mfma\w*", code)) == {"v_mfma_f32_32x32x2_f32"}, name
 
 
 def test_kernel_digests_written_by_build():

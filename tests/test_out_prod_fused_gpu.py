@@ -1,0 +1,173 @@
+"""GPU checks of out_prod with the dequantization fused into the GEMM
+(dq4_out_prod_fused).
+
+llama.cpp PR "cuda: out_prod dequantizes a 2D weight in row blocks": the
+approving review names the fused dequant-in-GEMM route as the follow-on of
+the row-blocked path.  The sum is the same, dst[i][j] = sum_r B[r][i] W[r][j],
+with the weight decoded inside the kernel.
+
+Two kinds of check:
+* the decode itself, bit for bit: with src1 a selection matrix (B[r][i] = 1
+  for one row r per column i, else 0) every dst element is one exact product
+  1 * W[r][j] plus exact zeros, so dst row i must equal the oracle's F32 row r
+  of the weight exactly -- whatever the summation order or split;
+* the sums against the oracle's weight times src1 in float64, within the
+  FP32 summation bound gamma_K * sum_r |B[r][i]| |W[r][j]| (any order, any
+  fusing), over the PR's worked example, the output head, ragged tiles, and
+  every split the workspace allows; the result is also checked to be
+  deterministic and to agree with the row-blocked route within twice the
+  bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import block_wise_bit_amd as dq4
+from block_wise_bit_amd import inputs
+from gpu_util import check_sum_bound, oracle_bits, out_prod_reference, say
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from libs import ensure_hip_library
+    ensure_hip_library()
+
+
+def _src1(b, transposed):
+    return torch.from_numpy(np.ascontiguousarray(b.T) if transposed else b).cuda()
+
+
+# (n_rows, n_cols, blocksize, format): aligned rows (n_cols % 8 == 0), ragged
+# tiles (n_cols % 128 != 0), blocks spanning rows (n_cols % blocksize != 0),
+# and odd widths (the byte path)
+DECODE_LAYOUTS = [
+    (300, 384, 64, "nf4"),
+    (301, 200, 64, "fp4"),
+    (257, 200, 32, "nf4"),
+    (130, 1000, 128, "nf4"),
+    (99, 101, 32, "fp4"),
+    (90, 333, 256, "nf4"),
+    (70, 4104, 4096, "nf4"),
+]
+
+
+@pytest.mark.parametrize("layout", DECODE_LAYOUTS, ids=lambda l: "x".join(map(str, l)))
+@pytest.mark.parametrize("transposed", [False, True])
+def test_in_kernel_decode_is_bit_exact(layout, transposed):
+    n_rows, n_cols, bs, fmt = layout
+    m = 70 if n_rows >= 70 else n_rows      # two i-tiles, the second ragged
+    x = inputs.make_inputs(n_rows * n_cols, bs, fmt, -0.1, seed=n_rows * 7 + n_cols,
+                           n_rows=n_rows, n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(n_cols))
+    sel = rng.choice(n_rows, m, replace=False)
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    for ws in (None, torch.empty(0, device="cuda")):
+        say(f"fused decode {layout} transposed={transposed} "
+            f"workspace={'preferred' if ws is None else 'none'}")
+        y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                                   blocksize=bs, src1=_src1(b, transposed),
+                                   src1_transposed=transposed, workspace=ws).cpu().numpy()
+        bad = np.argwhere(y != w[sel])
+        assert bad.size == 0, f"first mismatch at (i, j) = {bad[0]}: {y[tuple(bad[0])]!r} " \
+                              f"vs {w[sel][tuple(bad[0])]!r}"
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+def test_three_blocks_600000_rows_at_256_columns(transposed):
+    """The PR's worked example (600 000 rows, 256 columns, m = 8), both src1
+    orientations, dst prefilled with NaN."""
+    n_rows, n_cols, m = 600_000, 256, 8
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=600_000, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(1))
+    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    dst = torch.full((m, n_cols), float("nan"), dtype=torch.float32, device="cuda")
+    y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                               blocksize=64, src1=_src1(b, transposed),
+                               src1_transposed=transposed, dst=dst)
+    exact, mag = out_prod_reference(x, n_rows, n_cols, b)
+    check_sum_bound(y.cpu().numpy(), exact, mag, n_rows, f"600000x256 transposed={transposed}")
+
+
+def test_output_head_both_orientations_and_against_the_blocked_route():
+    """The 151936 x 5376 output head at m = 16 in both orientations; the fused
+    and the row-blocked results agree within twice the summation bound."""
+    wl = inputs.OUTPUT_HEAD
+    x = wl.inputs()
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(3))
+    m = 16
+    b = rng.standard_normal((wl.n_rows, m)).astype(np.float32)
+    exact, mag = out_prod_reference(x, wl.n_rows, wl.n_cols, b)
+    for transposed in (False, True):
+        src1 = _src1(b, transposed)
+        kw = dict(offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols, blocksize=64,
+                  src1=src1, src1_transposed=transposed)
+        fused = dq4.dq4_out_prod_fused(**dev, **kw).cpu().numpy()
+        check_sum_bound(fused, exact, mag, wl.n_rows, f"output head fused transposed={transposed}")
+        blocked = dq4.dq4_out_prod_rows(**dev, **kw).cpu().numpy()
+        check_sum_bound(fused, blocked.astype(np.float64), mag, wl.n_rows,
+                        "fused vs blocked", factor=2.0)
+
+
+def test_ragged_tiles_every_split_and_determinism():
+    """m = 150 (three i-tiles, the last ragged), n_cols = 200 (two j-tiles,
+    blocks of 64 spanning rows), with no workspace (one split), a workspace of
+    two partials, and the preferred one; each result is within the bound, and
+    a repeated call gives the same bits."""
+    n_rows, n_cols, m = 3000, 200, 150
+    x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", 0.1, seed=3000, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(5))
+    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    src1 = _src1(b, False)
+    exact, mag = out_prod_reference(x, n_rows, n_cols, b)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    say(f"preferred workspace {preferred} bytes = {preferred // (4 * m * n_cols)} partials")
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64, src1=src1)
+    for ws in (torch.empty(0, device="cuda"), torch.empty(2 * m * n_cols, device="cuda"), None):
+        y1 = dq4.dq4_out_prod_fused(**dev, **kw, workspace=ws).cpu().numpy()
+        y2 = dq4.dq4_out_prod_fused(**dev, **kw, workspace=ws).cpu().numpy()
+        what = "workspace " + ("preferred" if ws is None else f"{ws.numel() * 4} bytes")
+        check_sum_bound(y1, exact, mag, n_rows, what)
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), f"{what}: not deterministic"
+
+
+def test_edge_cases():
+    """Odd width on the byte path with a padded src1 (ld > m), the empty sum
+    (n_rows = 0 writes zeros), an empty dst, and a mistyped workspace."""
+    n_rows, n_cols, m = 37, 101, 3
+    x = inputs.make_inputs(n_rows * n_cols, 32, "nf4", 0.1, seed=37, n_rows=n_rows, n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(4))
+    padded = rng.standard_normal((n_rows, m + 5)).astype(np.float32)
+    src1 = torch.from_numpy(padded).cuda()[:, :m]          # ld = m + 5
+    exact, mag = out_prod_reference(x, n_rows, n_cols, padded[:, :m])
+    y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                               blocksize=32, src1=src1)
+    check_sum_bound(y.cpu().numpy(), exact, mag, n_rows, "37x101 padded src1")
+    empty = torch.empty((0, m), dtype=torch.float32, device="cuda")
+    dst = torch.full((m, n_cols), 5.0, dtype=torch.float32, device="cuda")
+    y = dq4.dq4_out_prod_fused(**dev, offset=0.0, n_rows=0, n_cols=n_cols, blocksize=32,
+                               src1=empty, dst=dst)
+    assert (y.cpu() == 0).all()
+    no_cols = torch.empty((n_rows, 0), dtype=torch.float32, device="cuda")
+    y = dq4.dq4_out_prod_fused(**dev, offset=0.0, n_rows=n_rows, n_cols=n_cols, blocksize=32,
+                               src1=no_cols)
+    assert y.shape == (0, n_cols)
+    with pytest.raises(ValueError):
+        dq4.dq4_out_prod_fused(**dev, offset=0.0, n_rows=n_rows, n_cols=n_cols, blocksize=32,
+                               src1=src1, workspace=torch.empty(8, dtype=torch.float16,
+                                                                device="cuda"))

@@ -21,13 +21,11 @@ import pytest
 
 import block_wise_bit_amd as dq4
 from block_wise_bit_amd import inputs
-from gpu_util import oracle_bits, say
+from gpu_util import check_sum_bound, out_prod_reference
 
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,29 +36,8 @@ def gpu():
     ensure_hip_library()
 
 
-def _reference(x, n_rows, n_cols, b_rows_by_m, chunk_rows=16384):
-    """float64 sum_r B[r][i] W[r][j] and sum_r |B[r][i]| |W[r][j]|, W from the oracle."""
-    m = b_rows_by_m.shape[1]
-    exact = np.zeros((m, n_cols))
-    mag = np.zeros((m, n_cols))
-    for r0 in range(0, n_rows, chunk_rows):
-        rows = min(chunk_rows, n_rows - r0)
-        w = oracle_bits(x, "f32", r0 * n_cols, rows * n_cols).view(np.float32)
-        w = w.reshape(rows, n_cols).astype(np.float64)
-        b = b_rows_by_m[r0:r0 + rows].astype(np.float64)
-        exact += b.T @ w
-        mag += np.abs(b).T @ np.abs(w)
-    return exact, mag
-
-
-def _check(got, exact, mag, K, what):
-    gamma = K * U / (1 - K * U)
-    err = np.abs(got.astype(np.float64) - exact)
-    bound = gamma * mag
-    worst = np.max(err / np.maximum(bound, 1e-300))
-    say(f"{what}: max |err| {err.max():.3e}, worst err/bound {worst:.3e}")
-    assert np.isfinite(got).all(), what
-    assert (err <= bound).all(), f"{what}: error above the FP32 summation bound"
+_reference = out_prod_reference
+_check = check_sum_bound
 
 
 @pytest.mark.parametrize("transposed", [False, True])
