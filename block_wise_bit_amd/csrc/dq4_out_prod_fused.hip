@@ -16,24 +16,30 @@
 // v_mfma_f32_32x32x2_f32.
 //
 // Design:
-//  * a workgroup (4 waves) owns a 64 x 128 tile of dst (64 values of i, the
-//    src1 columns; 128 of j, the weight columns) and one split of the rows r;
-//    each wave computes a 32 x 64 sub-tile as two 32 x 32 MFMA blocks that
-//    share their A operand;
+//  * a workgroup (4 waves) owns a kTileI x 128 tile of dst (kTileI values of
+//    i, the src1 columns: 128 once m >= 128, else 64; 128 of j, the weight
+//    columns) and one split of the rows r; its waves form a 2 x 2 grid, each
+//    computing 32 x 32 MFMA blocks that share their operands along i and j;
 //  * per stage of 16 weight rows every lane decodes 8 consecutive weight
 //    elements (one packed dword when n_cols % 8 == 0) with their one or two
-//    block scales, and stages 4 src1 values; the global loads of the next
-//    stage are issued before the MFMAs of the current one;
-//  * when the tiles alone cannot fill the GPU, the rows are split and each
-//    split writes its partial tile to the caller's workspace; a second kernel
-//    adds the partials in split order.  The result is deterministic for a
-//    given device and workspace size.
+//    block scales, and stages the tile's src1 values;
+//  * two LDS buffers: the waves decode the next stage into one while the
+//    MFMAs read the other, and the global loads of the stage after that are
+//    issued before the barrier, so each stage costs one barrier and its
+//    loads fly during the next stage's MFMAs;
+//  * the rows are split when that fills the GPU's resident workgroup slots
+//    (sized from the kernel's occupancy) better than the tiles alone; each
+//    split writes its partial tile to the caller's workspace, and a second
+//    kernel adds the partials in split order, so the result is deterministic
+//    for a given device and workspace size.
 // The FP32 sum order differs from the blocked route's library GEMM; both are
 // within the FP32 summation bound of the exact sum.
 
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "dq4.h"
 #include "dq4_device.h"
@@ -44,13 +50,11 @@ namespace dq4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileI = 64;          // dst rows (src1 columns) per workgroup
 constexpr int kTileJ = 128;         // dst columns (weight columns) per workgroup
 constexpr int kStage = 16;          // weight rows per LDS stage
 constexpr int kLdsW = kTileJ + 4;   // padded LDS row of decoded weights
-constexpr int kLdsB = kTileI + 4;   // padded LDS row of src1 values
-constexpr int kTargetGroupsPerCU = 8;
 constexpr int64_t kMinRowsPerSplit = 256;
+constexpr int64_t kMaxSplits = 64;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -71,39 +75,47 @@ struct FusedArgs {
     int log2_block;
     int tiles_i;
     int tiles_j;
-    int aligned8;            // n_cols % 8 == 0 and packed 4-byte aligned: a lane's 8
-                             // elements are one aligned packed dword
+};
+
+// Tile shape: a workgroup owns kTileI x kTileJ of dst; its 4 waves form a
+// 2 x 2 grid, each wave kWaveI x 64 as kBlocksI x 2 blocks of 32 x 32.
+template <int kTileI>
+struct Shape {
+    static constexpr int kWaveI = kTileI / 2;
+    static constexpr int kBlocksI = kWaveI / 32;
+    static constexpr int kLdsB = kTileI + 4;                 // padded LDS row of src1 values
+    static constexpr int kB = kStage * kTileI / kThreads;    // src1 values per lane and stage
 };
 
 // What one lane loads from HBM for one stage, before decoding it.
+template <int kTileI>
 struct StageLoad {
-    uint32_t packed4;   // 8 nibbles (aligned8) ...
+    uint32_t packed4;   // 8 nibbles (kAligned8) ...
     uint8_t bytes[8];   // ... or the byte holding each element (otherwise)
     uint32_t code_lo, code_hi;
     float absmax_lo, absmax_hi;
-    float b[4];
+    float b[Shape<kTileI>::kB];
 };
 
-template <bool kSrc1Transposed>
+// kAligned8: n_cols % 8 == 0 and packed 4-byte aligned, so a lane's 8
+// consecutive elements are one aligned packed dword and are all in range
+// together.
+template <int kTileI, bool kSrc1Transposed, bool kAligned8>
 __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
-                                           int64_t i0, int64_t j0, int t, StageLoad &ld)
+                                           int64_t i0, int64_t j0, int t,
+                                           StageLoad<kTileI> &ld)
 {
     // weight: row k0 + t / 16, columns j0 + (t % 16) * 8 .. + 7
     const int64_t r = k0 + (t >> 4);
     const int64_t j = j0 + (t & 15) * 8;
     const int lb = a.log2_block;
-    ld.code_lo = ld.code_hi = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        ld.bytes[q] = 0;
-    ld.absmax_lo = ld.absmax_hi = 0.0f;
-    ld.packed4 = 0;
     if (r < k_end && j < a.n_cols) {
         const int64_t e = r * a.n_cols + j;
-        const int64_t e_last = e + (min(a.n_cols - j, int64_t{8}) - 1);
-        if (a.aligned8) {
+        int64_t e_last = e + 7;
+        if constexpr (kAligned8) {
             ld.packed4 = *reinterpret_cast<const uint32_t *>(a.packed + (e >> 1));
         } else {
+            e_last = e + (min(a.n_cols - j, int64_t{8}) - 1);
 #pragma unroll
             for (int q = 0; q < 8; ++q)
                 ld.bytes[q] = e + q <= e_last ? a.packed[(e + q) >> 1] : 0;
@@ -114,29 +126,46 @@ __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64
         ld.code_hi = a.scale_codes[b_hi];
         ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
     }
-    // src1 values of the stage
+    constexpr int kB = Shape<kTileI>::kB;
     if constexpr (!kSrc1Transposed) {
-        // B[r][i] = src1[r * ld + i]: row k0 + t / 16, columns i0 + (t % 16) * 4 .. + 3
-        const int64_t rb = k0 + (t >> 4);
-        const int64_t ib = i0 + (t & 15) * 4;
+        // B[r][i] = src1[r * ld + i]: one stage row, kB consecutive columns
+        constexpr int kLanesPerRow = kTileI / kB;
+        const int64_t rb = k0 + t / kLanesPerRow;
+        const int64_t ib = i0 + (t % kLanesPerRow) * kB;
+        const float *p = a.src1 + rb * a.ld + ib;
+        if (rb < k_end && ib + kB <= a.m) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            ld.b[q] = (rb < k_end && ib + q < a.m) ? a.src1[rb * a.ld + ib + q] : 0.0f;
+            for (int q = 0; q < kB; ++q)
+                ld.b[q] = p[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < kB; ++q)
+                ld.b[q] = (rb < k_end && ib + q < a.m) ? p[q] : 0.0f;
+        }
     } else {
-        // B[r][i] = src1[i * ld + r]: column i0 + t / 4, rows k0 + (t % 4) * 4 .. + 3
-        const int64_t ib = i0 + (t >> 2);
-        const int64_t rb = k0 + (t & 3) * 4;
+        // B[r][i] = src1[i * ld + r]: one column i, kB consecutive stage rows
+        constexpr int kLanesPerCol = kStage / kB;
+        const int64_t ib = i0 + t / kLanesPerCol;
+        const int64_t rb = k0 + (t % kLanesPerCol) * kB;
+        const float *p = a.src1 + ib * a.ld + rb;
+        if (ib < a.m && rb + kB <= k_end) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            ld.b[q] = (rb + q < k_end && ib < a.m) ? a.src1[ib * a.ld + rb + q] : 0.0f;
+            for (int q = 0; q < kB; ++q)
+                ld.b[q] = p[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < kB; ++q)
+                ld.b[q] = (rb + q < k_end && ib < a.m) ? p[q] : 0.0f;
+        }
     }
 }
 
-template <bool kSrc1Transposed>
+template <int kTileI, bool kSrc1Transposed, bool kAligned8>
 __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
-                                             int64_t j0, int t, const StageLoad &ld,
+                                             int64_t j0, int t, const StageLoad<kTileI> &ld,
                                              const float *lds_scb, const float *lds_cb4,
-                                             float (*lds_w)[kLdsW], float (*lds_b)[kLdsB])
+                                             float (*lds_w)[kLdsW],
+                                             float (*lds_b)[Shape<kTileI>::kLdsB])
 {
     const int row = t >> 4, col = (t & 15) * 8;
     const int64_t r = k0 + row;
@@ -145,22 +174,27 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     if (r < k_end && j < a.n_cols) {
         const int lb = a.log2_block;
         const int64_t e = r * a.n_cols + j;
-        const int64_t n_valid = min(a.n_cols - j, int64_t{8});
         const float s_lo = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
         const float s_hi = block_scale(lds_scb[ld.code_hi], ld.absmax_hi, a.offset);
         // position of element e in its block; element e + q is in the next block
         // once off + q reaches the block size
         const uint32_t off = static_cast<uint32_t>(e & ((int64_t{1} << lb) - 1));
-        const uint32_t odd = static_cast<uint32_t>(e & 1);
+        if constexpr (kAligned8) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            uint32_t k;
-            if (a.aligned8)
-                k = (ld.packed4 >> (4 * q)) & 0xFu;
-            else
-                k = ((odd + q) & 1) ? (ld.bytes[q] >> 4) : (ld.bytes[q] & 0xFu);
-            const float s = ((off + q) >> lb) == 0 ? s_lo : s_hi;
-            v[q] = q < n_valid ? lds_cb4[k] * s : 0.0f;
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t k = (ld.packed4 >> (4 * q)) & 0xFu;
+                v[q] = lds_cb4[k] * (((off + q) >> lb) == 0 ? s_lo : s_hi);
+            }
+        } else {
+            const int64_t n_valid = min(a.n_cols - j, int64_t{8});
+            const uint32_t odd = static_cast<uint32_t>(e & 1);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t k =
+                    ((odd + q) & 1) ? (ld.bytes[q] >> 4) : (ld.bytes[q] & 0xFu);
+                const float s = ((off + q) >> lb) == 0 ? s_lo : s_hi;
+                v[q] = q < n_valid ? lds_cb4[k] * s : 0.0f;
+            }
         }
     } else {
 #pragma unroll
@@ -170,24 +204,68 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         lds_w[row][col + q] = v[q];
+    constexpr int kB = Shape<kTileI>::kB;
     if constexpr (!kSrc1Transposed) {
-        const int br = t >> 4, bc = (t & 15) * 4;
+        constexpr int kLanesPerRow = kTileI / kB;
+        const int br = t / kLanesPerRow, bc = (t % kLanesPerRow) * kB;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kB; ++q)
             lds_b[br][bc + q] = ld.b[q];
     } else {
-        const int bc = t >> 2, br = (t & 3) * 4;
+        constexpr int kLanesPerCol = kStage / kB;
+        const int bc = t / kLanesPerCol, br = (t % kLanesPerCol) * kB;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kB; ++q)
             lds_b[br + q][bc] = ld.b[q];
     }
 }
 
-template <bool kSrc1Transposed>
+// The MFMAs of one stage: acc[bi][bj] += A(i block bi) x W(j block bj) over
+// the stage's kStage rows, two rows per instruction; each step's operands
+// are read from LDS one step ahead of its MFMAs.
+template <int kTileI>
+__device__ __forceinline__ void mma_stage(const float (*lds_w)[kLdsW],
+                                          const float (*lds_b)[Shape<kTileI>::kLdsB], int wi,
+                                          int wj, int kl, int cl,
+                                          f32x16 (&acc)[Shape<kTileI>::kBlocksI][2])
+{
+    constexpr int kBI = Shape<kTileI>::kBlocksI;
+    const int ia = Shape<kTileI>::kWaveI * wi + cl, jw = 64 * wj + cl;
+    float av[2][kBI], wv[2][2];
+#pragma unroll
+    for (int bi = 0; bi < kBI; ++bi)
+        av[0][bi] = lds_b[kl][ia + 32 * bi];
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+        wv[0][bj] = lds_w[kl][jw + 32 * bj];
+#pragma unroll
+    for (int kk = 0; kk < kStage; kk += 2) {
+        const int cur = (kk >> 1) & 1, nxt = cur ^ 1;
+        if (kk + 2 < kStage) {
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                av[nxt][bi] = lds_b[kk + 2 + kl][ia + 32 * bi];
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+                wv[nxt][bj] = lds_w[kk + 2 + kl][jw + 32 * bj];
+        }
+#pragma unroll
+        for (int bi = 0; bi < kBI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cur][bi], wv[cur][bj],
+                                                                   acc[bi][bj], 0, 0, 0);
+    }
+}
+
+// Two LDS buffers: while the waves multiply one stage, they decode the next
+// into the other buffer, so one barrier per stage suffices.
+template <int kTileI, bool kSrc1Transposed, bool kAligned8>
 __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
 {
-    __shared__ float lds_w[kStage][kLdsW];
-    __shared__ float lds_b[kStage][kLdsB];
+    using S = Shape<kTileI>;
+    __shared__ float lds_w[2][kStage][kLdsW];
+    __shared__ float lds_b[2][kStage][S::kLdsB];
     __shared__ float lds_scb[256];
     __shared__ float lds_cb4[16];
 
@@ -205,44 +283,51 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
     if (t < 16)
         lds_cb4[t] = a.codebook4[t];
 
-    // wave sub-tile: i in [32 wi, 32 wi + 32), j in [64 wj, 64 wj + 64)
     const int wi = wave & 1, wj = wave >> 1;
     const int kl = lane >> 5, cl = lane & 31;
-    f32x16 acc0 = {}, acc1 = {};
-
-    StageLoad ld;
-    load_stage<kSrc1Transposed>(a, k_begin, k_end, i0, j0, t, ld);
-    __syncthreads();  // the codebooks are in LDS
-    for (int64_t k0 = k_begin; k0 < k_end; k0 += kStage) {
-        decode_stage<kSrc1Transposed>(a, k0, k_end, j0, t, ld, lds_scb, lds_cb4, lds_w, lds_b);
-        __syncthreads();
-        if (k0 + kStage < k_end)  // next stage's loads fly during this stage's MFMAs
-            load_stage<kSrc1Transposed>(a, k0 + kStage, k_end, i0, j0, t, ld);
+    f32x16 acc[S::kBlocksI][2];
 #pragma unroll
-        for (int kk = 0; kk < kStage; kk += 2) {
-            const float av = lds_b[kk + kl][32 * wi + cl];
-            const float w0 = lds_w[kk + kl][64 * wj + cl];
-            const float w1 = lds_w[kk + kl][64 * wj + 32 + cl];
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, w0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, w1, acc1, 0, 0, 0);
+    for (int bi = 0; bi < S::kBlocksI; ++bi)
+        acc[bi][0] = acc[bi][1] = f32x16{};
+
+    StageLoad<kTileI> ld;
+    load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, i0, j0, t, ld);
+    __syncthreads();  // the codebooks are in LDS
+    decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, j0, t, ld, lds_scb, lds_cb4,
+                                          lds_w[0], lds_b[0]);
+    if (k_begin + kStage < k_end)
+        load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin + kStage, k_end, i0, j0, t, ld);
+    __syncthreads();
+    // at the top of each pass: the stage at k0 is in buffer p, `ld` holds the
+    // stage at k0 + kStage (if any)
+    int p = 0;
+    for (int64_t k0 = k_begin; k0 < k_end; k0 += kStage, p ^= 1) {
+        mma_stage<kTileI>(lds_w[p], lds_b[p], wi, wj, kl, cl, acc);
+        if (k0 + kStage < k_end) {
+            decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0 + kStage, k_end, j0, t, ld, lds_scb,
+                                                  lds_cb4, lds_w[p ^ 1], lds_b[p ^ 1]);
+            if (k0 + 2 * kStage < k_end)
+                load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0 + 2 * kStage, k_end, i0, j0, t, ld);
         }
-        __syncthreads();  // LDS is rewritten by the next stage
+        __syncthreads();
     }
 
     // accumulator register v of lane l holds row 8 (v / 4) + 4 (l / 32) + v % 4,
-    // column l % 32 of the 32 x 32 block
+    // column l % 32 of its 32 x 32 block
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int64_t i = i0 + 32 * wi + 8 * (v >> 2) + 4 * kl + (v & 3);
-        const int64_t j = j0 + 64 * wj + cl;
-        if (i < a.m) {
-            if (j < a.n_cols)
-                out[i * a.n_cols + j] = acc0[v];
-            if (j + 32 < a.n_cols)
-                out[i * a.n_cols + j + 32] = acc1[v];
+    for (int bi = 0; bi < S::kBlocksI; ++bi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t i = i0 + S::kWaveI * wi + 32 * bi + 8 * (v >> 2) + 4 * kl + (v & 3);
+            const int64_t j = j0 + 64 * wj + cl;
+            if (i < a.m) {
+                if (j < a.n_cols)
+                    out[i * a.n_cols + j] = acc[bi][0][v];
+                if (j + 32 < a.n_cols)
+                    out[i * a.n_cols + j + 32] = acc[bi][1][v];
+            }
         }
-    }
 }
 
 // dst[x] = part[0][x] + part[1][x] + ... in split order
@@ -272,16 +357,64 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The split of the rows the fused kernel uses: enough workgroups to fill the
-// device, at least kMinRowsPerSplit rows each, and no more partial tiles than
-// max_partials (the workspace's capacity).  Returns the rows per split.
-int64_t rows_per_split(int64_t n_rows, int64_t tiles, int cus, int64_t max_partials)
+// The kernel for a launch: 128-row i-tiles once m fills them, else 64.
+struct Plan {
+    const void *kernel;
+    int tile_i;
+};
+
+template <int kTileI, bool kSrc1Transposed>
+const void *kernel_for(bool aligned8)
 {
-    int64_t splits = ceil_div(int64_t{kTargetGroupsPerCU} * cus, tiles);
-    splits = min(splits, ceil_div(n_rows, kMinRowsPerSplit));
-    splits = min(splits, max_partials);
-    if (splits < 1)
-        splits = 1;
+    return aligned8
+               ? reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, kSrc1Transposed, true>)
+               : reinterpret_cast<const void *>(
+                     &out_prod_fused_kernel<kTileI, kSrc1Transposed, false>);
+}
+
+Plan plan_for(int64_t m, bool transposed, bool aligned8)
+{
+    if (m >= 128)
+        return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
+                128};
+    return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64};
+}
+
+// Workgroups of `kernel` resident at once on one CU (at least 1).
+int resident_per_cu(const void *kernel)
+{
+    // the kernels use no dynamic LDS, so this depends on the kernel alone
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess ||
+        n < 1) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    return n;
+}
+
+// The split of the rows.  Workgroups all do the same work, so the kernel
+// takes ceil(groups / resident) rounds of resident workgroups; the split
+// count is the smallest that brings the fraction of occupied slots,
+// groups / (rounds * resident), within 2 % of the best reachable with at most
+// kMaxSplits splits, at least kMinRowsPerSplit rows per split, and no more
+// partial tiles than max_partials (the workspace's capacity).  Returns the
+// rows per split.
+int64_t rows_per_split(int64_t n_rows, int64_t tiles, int64_t resident, int64_t max_partials)
+{
+    const auto occupied = [&](int64_t splits) {
+        const int64_t groups = tiles * splits;
+        return static_cast<double>(groups) /
+               static_cast<double>(ceil_div(groups, resident) * resident);
+    };
+    int64_t s_max = min(ceil_div(n_rows, kMinRowsPerSplit), max_partials);
+    s_max = min(s_max, kMaxSplits);
+    double best = occupied(1);
+    for (int64_t s = 2; s <= s_max; ++s)
+        best = std::max(best, occupied(s));
+    int64_t splits = 1;
+    while (splits < s_max && occupied(splits) < 0.98 * best)
+        ++splits;
     return ceil_div(ceil_div(n_rows, splits), kStage) * kStage;
 }
 
@@ -301,14 +434,21 @@ extern "C" {
 int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m)
 {
     if (n_rows <= 0 || n_cols <= 0 || m <= 0 || n_cols > INT64_MAX / m ||
-        m * n_cols > INT64_MAX / 4 / 1024)
+        m * n_cols > INT64_MAX / 4 / dq4::kMaxSplits)
         return 0;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess)
         return 0;
-    const int64_t tiles = dq4::ceil_div(m, dq4::kTileI) * dq4::ceil_div(n_cols, dq4::kTileJ);
-    const int64_t rps = dq4::rows_per_split(n_rows, tiles, dq4::compute_units(device), 1024);
-    const int64_t splits = dq4::ceil_div(n_rows, rps);
+    // the largest split any variant of the kernel would take for this shape
+    int64_t splits = 1;
+    for (int v = 0; v < 4; ++v) {
+        const dq4::Plan plan = dq4::plan_for(m, (v & 1) != 0, (v & 2) != 0);
+        const int64_t tiles = dq4::ceil_div(m, plan.tile_i) * dq4::ceil_div(n_cols, dq4::kTileJ);
+        const int64_t resident =
+            int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan.kernel);
+        const int64_t rps = dq4::rows_per_split(n_rows, tiles, resident, dq4::kMaxSplits);
+        splits = std::max(splits, dq4::ceil_div(n_rows, rps));
+    }
     return splits > 1 ? splits * m * n_cols * 4 : 0;
 }
 
@@ -333,7 +473,9 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     if (!dst || n_cols > INT64_MAX / m || (n_rows > 0 && n_cols > INT64_MAX / n_rows))
         return DQ4_EINVAL;
     const int64_t count = m * n_cols;
-    const int64_t tiles_i = dq4::ceil_div(m, dq4::kTileI);
+    const bool aligned8 = n_cols % 8 == 0 && reinterpret_cast<uintptr_t>(packed) % 4 == 0;
+    const dq4::Plan plan = dq4::plan_for(m, src1_transposed != 0, aligned8);
+    const int64_t tiles_i = dq4::ceil_div(m, plan.tile_i);
     const int64_t tiles_j = dq4::ceil_div(n_cols, dq4::kTileJ);
     if (n_rows > 0) {
         if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 || !src1)
@@ -361,8 +503,9 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
         return e == hipSuccess ? DQ4_OK : dq4::hip_failed(e);
     }
     const int64_t max_partials = workspace_bytes / 4 / count;
-    const int64_t rps = dq4::rows_per_split(n_rows, tiles_i * tiles_j,
-                                            dq4::compute_units(device), max_partials);
+    const int64_t resident =
+        int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan.kernel);
+    const int64_t rps = dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
     const int64_t splits = dq4::ceil_div(n_rows, rps);
     const int64_t groups = splits * tiles_i * tiles_j;
     if (groups > 0x7FFFFFFF)
@@ -370,14 +513,10 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
 
     dq4::FusedArgs a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, src1,
                      splits > 1 ? workspace : dst, n_rows, n_cols, m, ld_src1, rps, offset,
-                     log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j),
-                     (n_cols % 8 == 0 && reinterpret_cast<uintptr_t>(packed) % 4 == 0) ? 1 : 0};
+                     log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j)};
     void *params[] = {&a};
-    const void *kernel =
-        src1_transposed ? reinterpret_cast<const void *>(&dq4::out_prod_fused_kernel<true>)
-                        : reinterpret_cast<const void *>(&dq4::out_prod_fused_kernel<false>);
-    e = hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(groups)), dim3(dq4::kThreads), params,
-                        0, s);
+    e = hipLaunchKernel(plan.kernel, dim3(static_cast<uint32_t>(groups)), dim3(dq4::kThreads),
+                        params, 0, s);
     if (e != hipSuccess)
         return dq4::hip_failed(e);
     if (splits > 1) {
