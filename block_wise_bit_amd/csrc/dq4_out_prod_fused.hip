@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dq4.h"
 #include "dq4_device.h"
@@ -56,6 +57,7 @@ constexpr int kLdsW = kTileJ + 4;   // padded LDS row of decoded weights
 constexpr int64_t kMinRowsPerSplit = 256;
 constexpr int64_t kMaxSplits = 64;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct FusedArgs {
@@ -77,14 +79,43 @@ struct FusedArgs {
     int tiles_j;
 };
 
-// Tile shape: a workgroup owns kTileI x kTileJ of dst; its 4 waves form a
-// 2 x 2 grid, each wave kWaveI x 64 as kBlocksI x 2 blocks of 32 x 32.
+// Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
+// it into kWavesI x kWavesJ sub-tiles of MFMA blocks.  kTileI = 64 or 128:
+// 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
+// instruction).  kTileI = 16, for decode-sized m: 1 x 4 waves of 16 x 16
+// blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction).
 template <int kTileI>
 struct Shape {
-    static constexpr int kWaveI = kTileI / 2;
-    static constexpr int kBlocksI = kWaveI / 32;
+    static constexpr bool kSmall = kTileI == 16;
+    static constexpr int kBlk = kSmall ? 16 : 32;           // MFMA block edge
+    static constexpr int kK = kSmall ? 4 : 2;               // weight rows per MFMA
+    static constexpr int kWavesI = kSmall ? 1 : 2;
+    static constexpr int kWaveI = kTileI / kWavesI;
+    static constexpr int kWaveJ = kTileJ / (4 / kWavesI);
+    static constexpr int kBlocksI = kWaveI / kBlk;
+    static constexpr int kBlocksJ = kWaveJ / kBlk;
+    static constexpr int kAccRegs = kBlk * kBlk / 64;        // accumulator values per lane
     static constexpr int kLdsB = kTileI + 4;                 // padded LDS row of src1 values
     static constexpr int kB = kStage * kTileI / kThreads;    // src1 values per lane and stage
+    using Acc = typename std::conditional<kSmall, f32x4, f32x16>::type;
+
+    // one MFMA: acc += A (kBlk x kK) x B (kK x kBlk); lane l holds A[l % kBlk][l / kBlk]
+    // and B[l / kBlk][l % kBlk]
+    __device__ static Acc mma(float a, float b, Acc acc)
+    {
+        if constexpr (kSmall)
+            return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    // the block row held by accumulator register v of lane l (its column is l % kBlk)
+    __device__ static int acc_row(int v, int l)
+    {
+        if constexpr (kSmall)
+            return 4 * (l >> 4) + v;
+        else
+            return 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    }
 };
 
 // What one lane loads from HBM for one stage, before decoding it.
@@ -221,40 +252,39 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
 }
 
 // The MFMAs of one stage: acc[bi][bj] += A(i block bi) x W(j block bj) over
-// the stage's kStage rows, two rows per instruction; each step's operands
+// the stage's kStage rows, kK rows per instruction; each step's operands
 // are read from LDS one step ahead of its MFMAs.
 template <int kTileI>
-__device__ __forceinline__ void mma_stage(const float (*lds_w)[kLdsW],
-                                          const float (*lds_b)[Shape<kTileI>::kLdsB], int wi,
-                                          int wj, int kl, int cl,
-                                          f32x16 (&acc)[Shape<kTileI>::kBlocksI][2])
+__device__ __forceinline__ void mma_stage(
+    const float (*lds_w)[kLdsW], const float (*lds_b)[Shape<kTileI>::kLdsB], int wi, int wj,
+    int kl, int cl,
+    typename Shape<kTileI>::Acc (&acc)[Shape<kTileI>::kBlocksI][Shape<kTileI>::kBlocksJ])
 {
-    constexpr int kBI = Shape<kTileI>::kBlocksI;
-    const int ia = Shape<kTileI>::kWaveI * wi + cl, jw = 64 * wj + cl;
-    float av[2][kBI], wv[2][2];
+    using S = Shape<kTileI>;
+    const int ia = S::kWaveI * wi + cl, jw = S::kWaveJ * wj + cl;
+    float av[2][S::kBlocksI], wv[2][S::kBlocksJ];
 #pragma unroll
-    for (int bi = 0; bi < kBI; ++bi)
-        av[0][bi] = lds_b[kl][ia + 32 * bi];
+    for (int bi = 0; bi < S::kBlocksI; ++bi)
+        av[0][bi] = lds_b[kl][ia + S::kBlk * bi];
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
-        wv[0][bj] = lds_w[kl][jw + 32 * bj];
+    for (int bj = 0; bj < S::kBlocksJ; ++bj)
+        wv[0][bj] = lds_w[kl][jw + S::kBlk * bj];
 #pragma unroll
-    for (int kk = 0; kk < kStage; kk += 2) {
-        const int cur = (kk >> 1) & 1, nxt = cur ^ 1;
-        if (kk + 2 < kStage) {
+    for (int kk = 0; kk < kStage; kk += S::kK) {
+        const int cur = (kk / S::kK) & 1, nxt = cur ^ 1;
+        if (kk + S::kK < kStage) {
 #pragma unroll
-            for (int bi = 0; bi < kBI; ++bi)
-                av[nxt][bi] = lds_b[kk + 2 + kl][ia + 32 * bi];
+            for (int bi = 0; bi < S::kBlocksI; ++bi)
+                av[nxt][bi] = lds_b[kk + S::kK + kl][ia + S::kBlk * bi];
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
-                wv[nxt][bj] = lds_w[kk + 2 + kl][jw + 32 * bj];
+            for (int bj = 0; bj < S::kBlocksJ; ++bj)
+                wv[nxt][bj] = lds_w[kk + S::kK + kl][jw + S::kBlk * bj];
         }
 #pragma unroll
-        for (int bi = 0; bi < kBI; ++bi)
+        for (int bi = 0; bi < S::kBlocksI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
-                acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cur][bi], wv[cur][bj],
-                                                                   acc[bi][bj], 0, 0, 0);
+            for (int bj = 0; bj < S::kBlocksJ; ++bj)
+                acc[bi][bj] = S::mma(av[cur][bi], wv[cur][bj], acc[bi][bj]);
     }
 }
 
@@ -283,12 +313,14 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
     if (t < 16)
         lds_cb4[t] = a.codebook4[t];
 
-    const int wi = wave & 1, wj = wave >> 1;
-    const int kl = lane >> 5, cl = lane & 31;
-    f32x16 acc[S::kBlocksI][2];
+    const int wi = wave % S::kWavesI, wj = wave / S::kWavesI;
+    const int kl = lane / S::kBlk, cl = lane % S::kBlk;
+    typename S::Acc acc[S::kBlocksI][S::kBlocksJ];
 #pragma unroll
     for (int bi = 0; bi < S::kBlocksI; ++bi)
-        acc[bi][0] = acc[bi][1] = f32x16{};
+#pragma unroll
+        for (int bj = 0; bj < S::kBlocksJ; ++bj)
+            acc[bi][bj] = typename S::Acc{};
 
     StageLoad<kTileI> ld;
     load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, i0, j0, t, ld);
@@ -312,20 +344,19 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
         __syncthreads();
     }
 
-    // accumulator register v of lane l holds row 8 (v / 4) + 4 (l / 32) + v % 4,
-    // column l % 32 of its 32 x 32 block
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
 #pragma unroll
     for (int bi = 0; bi < S::kBlocksI; ++bi)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t i = i0 + S::kWaveI * wi + 32 * bi + 8 * (v >> 2) + 4 * kl + (v & 3);
-            const int64_t j = j0 + 64 * wj + cl;
-            if (i < a.m) {
+        for (int v = 0; v < S::kAccRegs; ++v) {
+            const int64_t i = i0 + S::kWaveI * wi + S::kBlk * bi + S::acc_row(v, lane);
+            if (i >= a.m)
+                continue;
+#pragma unroll
+            for (int bj = 0; bj < S::kBlocksJ; ++bj) {
+                const int64_t j = j0 + S::kWaveJ * wj + S::kBlk * bj + cl;
                 if (j < a.n_cols)
-                    out[i * a.n_cols + j] = acc[bi][0][v];
-                if (j + 32 < a.n_cols)
-                    out[i * a.n_cols + j + 32] = acc[bi][1][v];
+                    out[i * a.n_cols + j] = acc[bi][bj][v];
             }
         }
 }
@@ -357,7 +388,8 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: 128-row i-tiles once m fills them, else 64.
+// The kernel for a launch: 128-row i-tiles once m fills them, 16-row ones for
+// decode-sized m, else 64.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -377,6 +409,9 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
     if (m >= 128)
         return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
                 128};
+    if (m <= 16)
+        return {transposed ? kernel_for<16, true>(aligned8) : kernel_for<16, false>(aligned8),
+                16};
     return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64};
 }
 

@@ -60,9 +60,11 @@ DECODE_LAYOUTS = [
 
 @pytest.mark.parametrize("layout", DECODE_LAYOUTS, ids=lambda l: "x".join(map(str, l)))
 @pytest.mark.parametrize("transposed", [False, True])
-def test_in_kernel_decode_is_bit_exact(layout, transposed):
+@pytest.mark.parametrize("m", [70, 16, 5])
+def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
+    """m = 70: two 64-row i-tiles, the second ragged; m = 16 and 5: the 16-row
+    tiles of the 16 x 16 x 4 matrix instruction, full and ragged."""
     n_rows, n_cols, bs, fmt = layout
-    m = 70 if n_rows >= 70 else n_rows      # two i-tiles, the second ragged
     x = inputs.make_inputs(n_rows * n_cols, bs, fmt, -0.1, seed=n_rows * 7 + n_cols,
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
@@ -72,7 +74,7 @@ def test_in_kernel_decode_is_bit_exact(layout, transposed):
     b[sel, np.arange(m)] = 1.0
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
     for ws in (None, torch.empty(0, device="cuda")):
-        say(f"fused decode {layout} transposed={transposed} "
+        say(f"fused decode {layout} m={m} transposed={transposed} "
             f"workspace={'preferred' if ws is None else 'none'}")
         y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
                                    blocksize=bs, src1=_src1(b, transposed),
@@ -171,3 +173,42 @@ def test_edge_cases():
         dq4.dq4_out_prod_fused(**dev, offset=0.0, n_rows=n_rows, n_cols=n_cols, blocksize=32,
                                src1=src1, workspace=torch.empty(8, dtype=torch.float16,
                                                                 device="cuda"))
+
+
+def test_graph_capture_replays_with_splits():
+    """The fused route -- kernel plus the reduction over row splits -- captured
+    in a HIP graph and replayed several times, with new src1 values written
+    eagerly between replays: every replay equals an eager call on the same
+    src1 bit for bit (the result is deterministic for a given workspace)."""
+    n_rows, n_cols, m = 20000, 384, 32
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=20000, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    assert preferred > 0, "this shape should split its rows"
+    ws = torch.empty(preferred // 4, dtype=torch.float32, device="cuda")
+    src1 = torch.empty((n_rows, m), dtype=torch.float32, device="cuda")
+    dst = torch.empty((m, n_cols), dtype=torch.float32, device="cuda")
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64, src1=src1,
+              workspace=ws)
+    g_rand = torch.Generator(device="cuda").manual_seed(11)
+    src1.normal_(generator=g_rand)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the path outside capture
+        dq4.dq4_out_prod_fused(**dev, **kw, dst=dst)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dq4.dq4_out_prod_fused(**dev, **kw, dst=dst)
+    for rep in range(4):
+        src1.normal_(generator=g_rand)      # eager work between replays
+        dst.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = dst.clone()
+        want = dq4.dq4_out_prod_fused(**dev, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"replay {rep}"
