@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "dq4.h"
@@ -389,10 +390,11 @@ int64_t ceil_div(int64_t a, int64_t b)
 }
 
 // The kernel for a launch: 128-row i-tiles once m fills them, 16-row ones for
-// decode-sized m, else 64.
+// decode-sized m, else 64.  `variant` (0..11) indexes the instantiation.
 struct Plan {
     const void *kernel;
     int tile_i;
+    int variant;
 };
 
 template <int kTileI, bool kSrc1Transposed>
@@ -406,25 +408,40 @@ const void *kernel_for(bool aligned8)
 
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
+    const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
     if (m >= 128)
         return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
-                128};
+                128, 8 + sub};
     if (m <= 16)
         return {transposed ? kernel_for<16, true>(aligned8) : kernel_for<16, false>(aligned8),
-                16};
-    return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64};
+                16, sub};
+    return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64,
+            4 + sub};
 }
 
-// Workgroups of `kernel` resident at once on one CU (at least 1).
-int resident_per_cu(const void *kernel)
+constexpr int kVariants = 12;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident[kMaxDevices][kVariants];
+
+// Workgroups of the plan's kernel resident at once on one CU of `device` (at
+// least 1), asked of the runtime once per device and kernel.  The kernels use
+// no dynamic LDS, so the answer depends on the kernel alone.
+int resident_per_cu(const Plan &plan, int device)
 {
-    // the kernels use no dynamic LDS, so this depends on the kernel alone
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess ||
+    std::atomic<int> *slot = device >= 0 && device < kMaxDevices
+                                 ? &g_resident[device][plan.variant]
+                                 : nullptr;
+    int n = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (n > 0)
+        return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, plan.kernel, kThreads, 0) !=
+            hipSuccess ||
         n < 1) {
         (void)hipGetLastError();
-        n = 1;
+        return 1;  // not cached: the next call asks again
     }
+    if (slot)
+        slot->store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -480,7 +497,7 @@ int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64
         const dq4::Plan plan = dq4::plan_for(m, (v & 1) != 0, (v & 2) != 0);
         const int64_t tiles = dq4::ceil_div(m, plan.tile_i) * dq4::ceil_div(n_cols, dq4::kTileJ);
         const int64_t resident =
-            int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan.kernel);
+            int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan, device);
         const int64_t rps = dq4::rows_per_split(n_rows, tiles, resident, dq4::kMaxSplits);
         splits = std::max(splits, dq4::ceil_div(n_rows, rps));
     }
@@ -539,7 +556,7 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     }
     const int64_t max_partials = workspace_bytes / 4 / count;
     const int64_t resident =
-        int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan.kernel);
+        int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan, device);
     const int64_t rps = dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
     const int64_t splits = dq4::ceil_div(n_rows, rps);
     const int64_t groups = splits * tiles_i * tiles_j;
