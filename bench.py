@@ -12,8 +12,10 @@ Prints ONE JSON line (rank 0, one GPU):
   value      = algorithmic bytes per step / wall-clock time per step, in GB/s
   roofline   = the kernel's achieved bandwidth from HIP events on its stream
                against MI355X's 8 TB/s HBM peak, and the HBM traffic measured
-               by rocprofv3 counters (profiles/), when they match this source
-  cpu_baseline = the CPU oracle (single thread) on the same inputs
+               by rocprofv3 counters (profiles/), while the built kernel's
+               instruction digest matches the one the counters were taken on
+  cpu_baseline = the CPU oracle on the same inputs, on the host's threads over
+               disjoint element ranges (single_core inside: on one thread)
 Timing protocol after the bitsandbytes issue's evidence plan ("B300 evidence
 plan"): >= 20 warmups, 7 timed batches of inner launches, every batch sample
 reported with median, p10 and p90.
