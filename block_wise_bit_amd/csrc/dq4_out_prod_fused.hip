@@ -254,7 +254,9 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
 
 // The MFMAs of one stage: acc[bi][bj] += A(i block bi) x W(j block bj) over
 // the stage's kStage rows, kK rows per instruction; each step's operands
-// are read from LDS one step ahead of its MFMAs.
+// are read from LDS one step ahead of its MFMAs.  (The raised wave priority
+// around this call is a scheduling hint within the kernel, not a stream
+// priority.)
 template <int kTileI>
 __device__ __forceinline__ void mma_stage(
     const float (*lds_w)[kLdsW], const float (*lds_b)[Shape<kTileI>::kLdsB], int wi, int wj,
@@ -286,6 +288,12 @@ __device__ __forceinline__ void mma_stage(
 #pragma unroll
             for (int bj = 0; bj < S::kBlocksJ; ++bj)
                 acc[bi][bj] = S::mma(av[cur][bi], wv[cur][bj], acc[bi][bj]);
+        if (kk + S::kK < kStage) {
+            // keep the next step's LDS reads ahead of this step's MFMAs (the
+            // compiler otherwise issues them just before their use)
+            __builtin_amdgcn_sched_group_barrier(0x100, S::kBlocksI + S::kBlocksJ, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, S::kBlocksI * S::kBlocksJ, 0);  // MFMA
+        }
     }
 }
 
@@ -335,7 +343,11 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
     // stage at k0 + kStage (if any)
     int p = 0;
     for (int64_t k0 = k_begin; k0 < k_end; k0 += kStage, p ^= 1) {
+        // a wave issuing MFMAs goes first among the SIMD's waves, so the matrix
+        // unit is fed while other waves decode (~2 % at m >= 512)
+        __builtin_amdgcn_s_setprio(1);
         mma_stage<kTileI>(lds_w[p], lds_b[p], wi, wj, kl, cl, acc);
+        __builtin_amdgcn_s_setprio(0);
         if (k0 + kStage < k_end) {
             decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0 + kStage, k_end, j0, t, ld, lds_scb,
                                                   lds_cb4, lds_w[p ^ 1], lds_b[p ^ 1]);
