@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         Word w[kUnits];
 #pragma unroll
         for (int u = 0; u < kUnits; ++u)
-            w[u] = load_packed<OUT>(words + u0 + u * kThreads + t);
+            w[u] = load_packed<OUT>(tile_word<OUT, kUnits>(words + u0, u, t));
 
         // 2. metadata of the outer blocks this tile touches, one block per lane
         const int64_t e_tile = a.e0 + d0 * 8;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         const __amdgpu_buffer_rsrc_t dst = unit_buffer(a.out, u0, kUnits * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
-            const uint32_t ul = u * kThreads + t;
+            const uint32_t ul = tile_unit<OUT, kUnits>(u, t);
             const float s = lds_scale[(r + ul * E) >> lb];
             float v[E];
 #pragma unroll

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         Word w[kUnits];
 #pragma unroll
         for (int u = 0; u < kUnits; ++u)
-            w[u] = load_packed<OUT>(wp + u0 + u * kThreads + t);
+            w[u] = load_packed<OUT>(tile_word<OUT, kUnits>(wp + u0, u, t));
         const int64_t b0 = (d0 * 8) >> log2_block;
         const uint32_t r = static_cast<uint32_t>(d0 * 8 - (b0 << log2_block));
         const int n_blocks = static_cast<int>((r + kTileElems - 1) >> log2_block) + 1;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         const __amdgpu_buffer_rsrc_t dst = unit_buffer(out, u0, kUnits * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
-            const uint32_t ul = u * kThreads + t;
+            const uint32_t ul = tile_unit<OUT, kUnits>(u, t);
             const float s = lds_scale[(r + ul * E) >> log2_block];
             float v[E];
 #pragma unroll
