@@ -16,9 +16,10 @@
 //  * one workgroup of 256 lanes per tile of 4096 elements (2 KiB packed in,
 //    8 or 16 KiB out).  The tile is cut into "units" of 8 elements (one
 //    packed dword) for FP16/BF16 output or 4 elements (one packed 16-bit
-//    word) for FP32 output; lane t takes unit u * 256 + t, so each wavefront
-//    load is contiguous and each store instruction writes 64 x 16 contiguous
-//    bytes for every output type.  One tile per workgroup, in dispatch order,
+//    word) for FP32 output; lane t takes unit u * 256 + t (FP16/BF16) or one
+//    of its wave's contiguous run of units (FP32), so each wavefront load is
+//    contiguous and each store instruction writes 64 x 16 contiguous bytes
+//    for every output type.  One tile per workgroup, in dispatch order,
 //    keeps the set of addresses being written compact; on MI355X this writes
 //    markedly faster than a persistent grid-stride loop, and 4096-element
 //    tiles measured faster than 2048 (by ~45 %), 6144 (~0.3 %) and 8192
