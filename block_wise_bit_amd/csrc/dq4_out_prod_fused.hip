@@ -155,8 +155,12 @@ __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64
         const int64_t b_lo = e >> lb, b_hi = e_last >> lb;  // at most two blocks
         ld.code_lo = a.scale_codes[b_lo];
         ld.absmax_lo = a.nested_absmax[b_lo >> kNestedLog2];
-        ld.code_hi = a.scale_codes[b_hi];
-        ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
+        if constexpr (!kAligned8) {
+            // with kAligned8, e is a multiple of 8 and so is the block size
+            // (a power of two >= 32): the 8 elements share block b_lo
+            ld.code_hi = a.scale_codes[b_hi];
+            ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
+        }
     }
     constexpr int kB = Shape<kTileI>::kB;
     if constexpr (!kSrc1Transposed) {
@@ -204,20 +208,21 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     const int64_t j = j0 + col;
     float v[8];
     if (r < k_end && j < a.n_cols) {
-        const int lb = a.log2_block;
-        const int64_t e = r * a.n_cols + j;
         const float s_lo = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
-        const float s_hi = block_scale(lds_scb[ld.code_hi], ld.absmax_hi, a.offset);
-        // position of element e in its block; element e + q is in the next block
-        // once off + q reaches the block size
-        const uint32_t off = static_cast<uint32_t>(e & ((int64_t{1} << lb) - 1));
         if constexpr (kAligned8) {
+            // one block for all 8 elements (see load_stage)
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const uint32_t k = (ld.packed4 >> (4 * q)) & 0xFu;
-                v[q] = lds_cb4[k] * (((off + q) >> lb) == 0 ? s_lo : s_hi);
+                v[q] = lds_cb4[k] * s_lo;
             }
         } else {
+            const int lb = a.log2_block;
+            const int64_t e = r * a.n_cols + j;
+            const float s_hi = block_scale(lds_scb[ld.code_hi], ld.absmax_hi, a.offset);
+            // position of element e in its block; element e + q is in the next
+            // block once off + q reaches the block size
+            const uint32_t off = static_cast<uint32_t>(e & ((int64_t{1} << lb) - 1));
             const int64_t n_valid = min(a.n_cols - j, int64_t{8});
             const uint32_t odd = static_cast<uint32_t>(e & 1);
 #pragma unroll
