@@ -17,9 +17,14 @@
 //
 // Design:
 //  * a workgroup (4 waves) owns a kTileI x 128 tile of dst (kTileI values of
-//    i, the src1 columns: 128 once m >= 128, else 64; 128 of j, the weight
-//    columns) and one split of the rows r; its waves form a 2 x 2 grid, each
-//    computing 32 x 32 MFMA blocks that share their operands along i and j;
+//    i, the src1 columns: 256 once m >= 256, 128 once m >= 128, else 64 or,
+//    for decode-sized m, 16; 128 of j, the weight columns) and one split of
+//    the rows r; its waves form a 2 x 2 grid, each computing 32 x 32 MFMA
+//    blocks that share their operands along i and j.  The decode of a stage
+//    costs the same at every kTileI while the MFMAs grow with it, and on
+//    gfx950 vector instructions barely overlap FP32 MFMAs, so the widest
+//    tile that m fills is the fastest (256 rows: ~5 % over 128 at m >= 512,
+//    although its 128 accumulator registers leave one wave per SIMD);
 //  * per stage of 16 weight rows every lane decodes 8 consecutive weight
 //    elements (one packed dword when n_cols % 8 == 0) with their one or two
 //    block scales, and stages the tile's src1 values;
@@ -81,8 +86,8 @@ struct FusedArgs {
 };
 
 // Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
-// it into kWavesI x kWavesJ sub-tiles of MFMA blocks.  kTileI = 64 or 128:
-// 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
+// it into kWavesI x kWavesJ sub-tiles of MFMA blocks.  kTileI = 64, 128 or
+// 256: 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
 // instruction).  kTileI = 16, for decode-sized m: 1 x 4 waves of 16 x 16
 // blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction).
 template <int kTileI>
@@ -406,8 +411,8 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: 128-row i-tiles once m fills them, 16-row ones for
-// decode-sized m, else 64.  `variant` (0..11) indexes the instantiation.
+// The kernel for a launch: the widest i-tile m fills (256, 128), 16-row ones
+// for decode-sized m, else 64.  `variant` (0..15) indexes the instantiation.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -426,6 +431,9 @@ const void *kernel_for(bool aligned8)
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
     const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
+    if (m >= 256)
+        return {transposed ? kernel_for<256, true>(aligned8) : kernel_for<256, false>(aligned8),
+                256, 12 + sub};
     if (m >= 128)
         return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
                 128, 8 + sub};
@@ -436,7 +444,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             4 + sub};
 }
 
-constexpr int kVariants = 12;
+constexpr int kVariants = 16;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

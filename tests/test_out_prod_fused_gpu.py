@@ -60,16 +60,18 @@ DECODE_LAYOUTS = [
 
 @pytest.mark.parametrize("layout", DECODE_LAYOUTS, ids=lambda l: "x".join(map(str, l)))
 @pytest.mark.parametrize("transposed", [False, True])
-@pytest.mark.parametrize("m", [70, 16, 5])
+@pytest.mark.parametrize("m", [300, 150, 70, 16, 5])
 def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
-    """m = 70: two 64-row i-tiles, the second ragged; m = 16 and 5: the 16-row
-    tiles of the 16 x 16 x 4 matrix instruction, full and ragged."""
+    """m = 300: two 256-row i-tiles, the second ragged; m = 150: two 128-row
+    i-tiles; m = 70: two 64-row i-tiles, the second ragged; m = 16 and 5: the
+    16-row tiles of the 16 x 16 x 4 matrix instruction, full and ragged.
+    Columns select weight rows with repeats when m exceeds the row count."""
     n_rows, n_cols, bs, fmt = layout
     x = inputs.make_inputs(n_rows * n_cols, bs, fmt, -0.1, seed=n_rows * 7 + n_cols,
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
     rng = np.random.Generator(np.random.PCG64(n_cols))
-    sel = rng.choice(n_rows, m, replace=False)
+    sel = rng.choice(n_rows, m, replace=m > n_rows)
     b = np.zeros((n_rows, m), np.float32)
     b[sel, np.arange(m)] = 1.0
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
@@ -123,12 +125,14 @@ def test_output_head_both_orientations_and_against_the_blocked_route():
                         "fused vs blocked", factor=2.0)
 
 
-def test_ragged_tiles_every_split_and_determinism():
-    """m = 150 (three i-tiles, the last ragged), n_cols = 200 (two j-tiles,
-    blocks of 64 spanning rows), with no workspace (one split), a workspace of
-    two partials, and the preferred one; each result is within the bound, and
-    a repeated call gives the same bits."""
-    n_rows, n_cols, m = 3000, 200, 150
+@pytest.mark.parametrize("m", [150, 300])
+def test_ragged_tiles_every_split_and_determinism(m):
+    """m = 150 (two 128-row i-tiles, the last ragged) and m = 300 (two 256-row
+    i-tiles, the last ragged), n_cols = 200 (two j-tiles, blocks of 64
+    spanning rows), with no workspace (one split), a workspace of two
+    partials, and the preferred one; each result is within the bound, and a
+    repeated call gives the same bits."""
+    n_rows, n_cols = 3000, 200
     x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", 0.1, seed=3000, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
