@@ -634,6 +634,44 @@ def configs_bench(args, torch, dq4, inputs) -> int:
     return 0
 
 
+def launch_trace(args, torch, dq4, inputs) -> int:
+    """Three phases for a launch/allocation trace (rocprofv3 --kernel-trace
+    --hip-trace --memory-allocation-trace): 10 fused calls into the caller's
+    output, 10 unfused calls with the caller's scale workspace, and 10
+    unfused calls where the binding allocates that workspace (torch's cache
+    emptied after each call).  Everything else is allocated up front; a
+    one-element torch add and a synchronization mark each phase boundary."""
+    n = 4096 * 4096
+    x = inputs.make_inputs(n, 64, "nf4", 0.03, seed=inputs.SEED_BASE + 1, n_rows=4096,
+                           n_cols=4096)
+    dev = dq4.to_device(x, "cuda:0")
+    out = torch.empty(n, dtype=torch.float16, device="cuda:0")
+    ws = torch.empty(dq4.dq4_unfused_workspace_bytes(n, 64) // 4, dtype=torch.float32,
+                     device="cuda:0")
+    marker = torch.zeros(1, device="cuda:0")
+    kw = dict(offset=float(x.offset), n=n, blocksize=64, out_dtype=torch.float16, out=out)
+    torch.cuda.synchronize()
+
+    def mark():
+        marker.add_(1.0)
+        torch.cuda.synchronize()
+    mark()
+    for _ in range(10):
+        dq4.dq4_nested_dequant(**dev, **kw)
+    mark()
+    for _ in range(10):
+        dq4.dq4_nested_dequant_unfused(**dev, **kw, scale_workspace=ws)
+    mark()
+    torch.cuda.empty_cache()
+    for _ in range(10):
+        dq4.dq4_nested_dequant_unfused(**dev, **kw)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    mark()
+    print(json.dumps({"launch_trace": "phases done", "n": n}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,6 +703,9 @@ def main() -> int:
                     help="instead of the benchmark, time every dequantization workload (square, "
                          "mid matrix, headline, block-size sweep, output-head window loop) "
                          "against the HBM roofline")
+    ap.add_argument("--launch-trace", action="store_true",
+                    help="instead of the benchmark, run the fused and unfused calls in marked "
+                         "phases for a rocprofv3 launch and allocation trace")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of MIB "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -698,6 +739,8 @@ def main() -> int:
         return int8_prep_bench(args, torch, dq4)
     if args.configs:
         return configs_bench(args, torch, dq4, inputs)
+    if args.launch_trace:
+        return launch_trace(args, torch, dq4, inputs)
 
     wl = inputs.HEADLINE
     n, bs = wl.n, wl.blocksize
