@@ -127,7 +127,8 @@ def test_validation_out_prod_fused(lib):
     assert call(dst=None) == dq4.DQ4_EINVAL
     assert call(blocksize=7) == dq4.DQ4_EUNSUPPORTED
     assert call(nested=128) == dq4.DQ4_EUNSUPPORTED
-    assert call(m=(1 << 31) * 128, ld=(1 << 31) * 128) == dq4.DQ4_EUNSUPPORTED  # > 2^31 - 1 tiles
+    # 256-row tiles at this m: 2^31 i-tiles, more than a grid can hold
+    assert call(m=(1 << 31) * 256, ld=(1 << 31) * 256) == dq4.DQ4_EUNSUPPORTED
     for args in ((0, 64, 8), (100, 0, 8), (100, 64, 0), (-1, 64, 8), (1 << 40, 1 << 40, 1 << 40)):
         assert lib.dq4_out_prod_fused_workspace_bytes(*args) == 0
 
