@@ -69,6 +69,24 @@ def measured_traffic():
     return s.get("hbm_bytes_per_launch")
 
 
+def run_env(torch) -> dict:
+    """Identity of what ran: software versions, the GPU, and a digest of the
+    library binary (the kernel digests identify each kernel's code)."""
+    import hashlib
+    lib = os.path.join(ROOT, "block_wise_bit_amd", "libdq4.so")
+    try:
+        with open(lib, "rb") as fh:
+            lib_digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+    except OSError:
+        lib_digest = None
+    props = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "library_sha256_16": lib_digest, "python": platform.python_version(),
+            "host_logical_cpus": os.cpu_count()}
+
+
 def percentile(xs, q):
     xs = sorted(xs)
     if not xs:
@@ -117,16 +135,22 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
     reads its packed weight from HBM, not from the last-level cache."""
     import math
 
+    all_dtypes = (("f16", torch.float16, 2), ("bf16", torch.bfloat16, 2),
+                  ("f32", torch.float32, 4))
+    # the primary matrix, then the odd-tail control (1-D, odd length: a packed
+    # tail nibble, a partial outer block and a partial nested group)
+    cases = [(rows, cols, all_dtypes, None) for rows, cols in PRIMARY_SHAPES]
+    cases.append((1, inputs.TAIL_SWEEP_N, all_dtypes[:1], "odd_tail"))
     cells = []
-    for rows, cols in PRIMARY_SHAPES:
+    for rows, cols, dtypes, control in cases:
         n = rows * cols
         for fmt in ("nf4", "fp4"):
             x = inputs.make_inputs(n, 64, fmt, -0.02, seed=inputs.SEED_BASE + 2, n_rows=rows,
                                    n_cols=cols)
-            for dt, tdt, ob in (("f16", torch.float16, 2), ("bf16", torch.bfloat16, 2),
-                                ("f32", torch.float32, 4)):
+            for dt, tdt, ob in dtypes:
                 alg = algorithmic_bytes(n, 64, ob)
-                n_sets = max(2, math.ceil(1.2e9 / alg), math.ceil(COLD_PACKED_BYTES / (n // 2)))
+                n_sets = max(2, math.ceil(1.2e9 / alg),
+                             math.ceil(COLD_PACKED_BYTES / ((n + 1) // 2)))
                 ws_len = dq4.dq4_unfused_workspace_bytes(n, 64) // 4
                 sets = [(dq4.to_device(x, "cuda:0"), torch.empty(n, dtype=tdt, device="cuda:0"),
                          torch.empty(ws_len, dtype=torch.float32, device="cuda:0"))
@@ -198,7 +222,8 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
                 del ref
                 med = {k: percentile(v, 0.5) for k, v in samples.items()}
                 f_med, u_med = med["fused"], med["unfused"]
-                cell = {"shape": f"{rows}x{cols}", "format": fmt, "out": dt,
+                cell = {"shape": f"{rows}x{cols}" if control is None else f"n={n}",
+                        "control": control, "format": fmt, "out": dt,
                         "fused_us": round(f_med, 2), "unfused_us": round(u_med, 2),
                         "speedup": round(u_med / f_med, 4),
                         "fused_p10_p90": [round(percentile(samples["fused"], q), 2)
@@ -222,22 +247,25 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
     def geomean(vals):
         return math.exp(sum(math.log(v) for v in vals) / len(vals))
 
-    primary = [c["speedup"] for c in cells if c["out"] in ("f16", "bf16")]
-    controls = [c["speedup"] for c in cells if c["out"] == "f32"]
-    eager = [c["eager_speedup"] for c in cells if c["out"] in ("f16", "bf16")]
+    main = [c for c in cells if c["control"] is None]
+    primary = [c["speedup"] for c in main if c["out"] in ("f16", "bf16")]
+    controls = [c["speedup"] for c in main if c["out"] == "f32"]
+    eager = [c["eager_speedup"] for c in main if c["out"] in ("f16", "bf16")]
+    odd_tail = {c["format"]: c["speedup"] for c in cells if c["control"] == "odd_tail"}
     all_equal = all(c["bit_equal"] for c in cells)
     print(json.dumps({
         "metric": "fused vs unfused nested dequant speedup, geomean over NF4/FP4 x FP16/BF16, "
                   "bs64, primary standalone matrix",
         "value": round(geomean(primary), 4), "unit": "x", "higher_is_better": True,
         "fp32_control_geomean": round(geomean(controls), 4),
+        "odd_tail_control_speedup": odd_tail,
         "eager_geomean": round(geomean(eager), 4),
         "timing": "device time per call from HIP-graph replays of `inner` calls, median of "
                   ">= 7 interleaved batches; eager_* = the same calls launched from Python",
         "min_primary_speedup": round(min(primary), 4),
         "fused_equals_unfused_bitwise": all_equal,
         "n_gpus": 1, "warmup": args.warmup, "data": "synthetic", "cells": cells,
-        "device": torch.cuda.get_device_name(0)}), flush=True)
+        "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
     return 0 if all_equal else 3
 
 
@@ -327,7 +355,7 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
         "roofline": {"bound": "mfma", "achieved": tflops["fused"], "peak": 157.3,
                      "unit": "TFLOP/s", "frac": round(tflops["fused"] / 157.3, 4)},
         "best_route_TFLOPs": best,
-        "device": torch.cuda.get_device_name(0)}), flush=True)
+        "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
     return 0
 
 
@@ -404,7 +432,7 @@ def linear_bench(args, torch, dq4, inputs) -> int:
                   "(geomean over forward/grad_A cells)",
         "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 4), "unit": "x",
         "higher_is_better": True, "n_gpus": 1, "data": "synthetic", "cells": cells,
-        "device": torch.cuda.get_device_name(0)}), flush=True)
+        "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
     return 0
 
 
@@ -471,9 +499,11 @@ def int8_prep_bench(args, torch, dq4) -> int:
         "metric": "LLM.int8 correction-operand preparation: one kernel vs the eager chain "
                   "(speedup, geomean)",
         "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 3), "unit": "x",
-        "higher_is_better": True, "min_speedup": min(sp), "median_speedup": sorted(sp)[len(sp) // 2],
+        "higher_is_better": True, "min_speedup": min(sp),
+        "median_speedup": sorted(sp)[len(sp) // 2],
         "all_bit_equal": all(c["bit_equal_to_eager"] for c in cells), "n_gpus": 1,
-        "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0)}),
+        "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0),
+        "env": run_env(torch)}),
         flush=True)
     return 0
 
@@ -618,8 +648,8 @@ def configs_bench(args, torch, dq4, inputs) -> int:
             "frac": round(alg_total / (med_loop * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "ideal_us": round(alg_total / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
             "per_window": win_cells,
-            "timing": "loop_us: 6 loops of the 13 launches replayed as one HIP graph, median of >= 7 "
-                      "replays; eager_loop_us and per_window: eager launches with one HIP "
+            "timing": "loop_us: 6 loops of the 13 launches replayed as one HIP graph, median "
+                      "of >= 7 replays; eager_loop_us and per_window: eager launches with one HIP "
                       "event after each window"}
     print(f"[configs] {wl.name}: {len(windows)} windows in {med_loop:.1f} us, "
           f"{head['GBps']} GB/s ({head['frac']:.3f})", file=sys.stderr, flush=True)
@@ -629,7 +659,8 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         "unit": "GB/s", "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
         "timing": "device time per call from HIP-graph replays over cycled cold input sets, "
                   "median of >= 7 batches",
-        "cells": cells, "output_head": head, "device": torch.cuda.get_device_name(0)}),
+        "cells": cells, "output_head": head, "device": torch.cuda.get_device_name(0),
+        "env": run_env(torch)}),
         flush=True)
     return 0
 
@@ -822,7 +853,7 @@ def main() -> int:
                       "p10": round(percentile(batch_us, 0.1), 3),
                       "p90": round(percentile(batch_us, 0.9), 3)},
         "kernel_isa_sha256_16": kernel_digest(),
-        "device": torch.cuda.get_device_name(0),
+        "device": torch.cuda.get_device_name(0), "env": run_env(torch),
         "cpu_baseline": None,
         "parity": None,
     }
