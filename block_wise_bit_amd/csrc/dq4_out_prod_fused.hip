@@ -23,8 +23,8 @@
 //    blocks that share their operands along i and j.  The decode of a stage
 //    costs the same at every kTileI while the MFMAs grow with it, and on
 //    gfx950 vector instructions barely overlap FP32 MFMAs, so the widest
-//    tile that m fills is the fastest (256 rows: ~5 % over 128 at m >= 512,
-//    although its 128 accumulator registers leave one wave per SIMD);
+//    tile that m fills is the fastest (256 rows: ~5 % over 128 at m >= 512;
+//    its 188 registers, 128 of them accumulators, leave two waves per SIMD);
 //  * per stage of 16 weight rows every lane decodes 8 consecutive weight
 //    elements (one packed dword when n_cols % 8 == 0) with their one or two
 //    block scales, and stages the tile's src1 values;
