@@ -17,14 +17,15 @@
 //
 // Design:
 //  * a workgroup (4 waves) owns a kTileI x 128 tile of dst (kTileI values of
-//    i, the src1 columns: 256 once m >= 256, 128 once m >= 128, else 64 or,
-//    for decode-sized m, 16; 128 of j, the weight columns) and one split of
-//    the rows r; its waves form a 2 x 2 grid, each computing 32 x 32 MFMA
-//    blocks that share their operands along i and j.  The decode of a stage
-//    costs the same at every kTileI while the MFMAs grow with it, and on
-//    gfx950 vector instructions barely overlap FP32 MFMAs, so the widest
-//    tile that m fills is the fastest (256 rows: ~5 % over 128 at m >= 512;
-//    its 188 registers, 128 of them accumulators, leave two waves per SIMD);
+//    i, the src1 columns: 256, 128 or 64, or 16 for decode-sized m; 128 of
+//    j, the weight columns) and one split of the rows r; its waves form a
+//    2 x 2 grid, each computing 32 x 32 MFMA blocks that share their
+//    operands along i and j.  The decode of a stage costs the same at every
+//    kTileI while the MFMAs grow with it, and on gfx950 vector instructions
+//    barely overlap FP32 MFMAs, so wider tiles cost less per row (256 rows:
+//    ~5 % over 128 at m >= 512; its 188 registers, 128 of them accumulators,
+//    leave two waves per SIMD); a ragged m pays for the padded rows of its
+//    last tile, so the width comes from a cost rule (tile_cost);
 //  * per stage of 16 weight rows every lane decodes 8 consecutive weight
 //    elements (one packed dword when n_cols % 8 == 0) with their one or two
 //    block scales, and stages the tile's src1 values;
@@ -411,8 +412,8 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: the widest i-tile m fills (256, 128), 16-row ones
-// for decode-sized m, else 64.  `variant` (0..15) indexes the instantiation.
+// The kernel for a launch: 16-row i-tiles for decode-sized m, else the width
+// of least tile_cost.  `variant` (0..15) indexes the instantiation.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -428,18 +429,33 @@ const void *kernel_for(bool aligned8)
                      &out_prod_fused_kernel<kTileI, kSrc1Transposed, false>);
 }
 
+// Relative work per dst row of each i-tile width, measured on the output head
+// with m a multiple of the width (FP32 TFLOP/s 128 / 109 / 93 at widths
+// 256 / 128 / 64): the decode cost of a stage is shared by more rows in a
+// wider tile.  A ragged m pays for its padded rows, so the width that
+// minimizes padded rows x relative cost wins.
+double tile_cost(int64_t m, int64_t tile_i)
+{
+    const double rel = tile_i == 256 ? 1.0 : tile_i == 128 ? 1.17 : 1.37;
+    return static_cast<double>(ceil_div(m, tile_i) * tile_i) * rel;
+}
+
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
     const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
-    if (m >= 256)
-        return {transposed ? kernel_for<256, true>(aligned8) : kernel_for<256, false>(aligned8),
-                256, 12 + sub};
-    if (m >= 128)
-        return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
-                128, 8 + sub};
     if (m <= 16)
         return {transposed ? kernel_for<16, true>(aligned8) : kernel_for<16, false>(aligned8),
                 16, sub};
+    int64_t best = 64;
+    for (const int64_t w : {128, 256})
+        if (tile_cost(m, w) < tile_cost(m, best))
+            best = w;
+    if (best == 256)
+        return {transposed ? kernel_for<256, true>(aligned8) : kernel_for<256, false>(aligned8),
+                256, 12 + sub};
+    if (best == 128)
+        return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
+                128, 8 + sub};
     return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64,
             4 + sub};
 }

@@ -62,10 +62,11 @@ DECODE_LAYOUTS = [
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("m", [300, 150, 70, 16, 5])
 def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
-    """m = 300: two 256-row i-tiles, the second ragged; m = 150: two 128-row
-    i-tiles; m = 70: two 64-row i-tiles, the second ragged; m = 16 and 5: the
-    16-row tiles of the 16 x 16 x 4 matrix instruction, full and ragged.
-    Columns select weight rows with repeats when m exceeds the row count."""
+    """Every i-tile width, each with a ragged last tile: m = 300 takes five
+    64-row tiles, m = 150 one 256-row tile, m = 70 one 128-row tile (the
+    widths the kernel's cost rule picks for them); m = 16 and 5 the 16-row
+    tiles of the 16 x 16 x 4 matrix instruction, full and ragged.  Columns
+    select weight rows with repeats when m exceeds the row count."""
     n_rows, n_cols, bs, fmt = layout
     x = inputs.make_inputs(n_rows * n_cols, bs, fmt, -0.1, seed=n_rows * 7 + n_cols,
                            n_rows=n_rows, n_cols=n_cols)
@@ -127,11 +128,11 @@ def test_output_head_both_orientations_and_against_the_blocked_route():
 
 @pytest.mark.parametrize("m", [150, 300])
 def test_ragged_tiles_every_split_and_determinism(m):
-    """m = 150 (two 128-row i-tiles, the last ragged) and m = 300 (two 256-row
-    i-tiles, the last ragged), n_cols = 200 (two j-tiles, blocks of 64
-    spanning rows), with no workspace (one split), a workspace of two
-    partials, and the preferred one; each result is within the bound, and a
-    repeated call gives the same bits."""
+    """m = 150 (one ragged 256-row i-tile) and m = 300 (five 64-row i-tiles,
+    the last ragged), n_cols = 200 (two j-tiles, blocks of 64 spanning rows),
+    with no workspace (one split), a workspace of two partials, and the
+    preferred one; each result is within the bound, and a repeated call gives
+    the same bits."""
     n_rows, n_cols = 3000, 200
     x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", 0.1, seed=3000, n_rows=n_rows,
                            n_cols=n_cols)
