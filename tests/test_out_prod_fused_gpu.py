@@ -217,3 +217,43 @@ def test_graph_capture_replays_with_splits():
         want = dq4.dq4_out_prod_fused(**dev, **kw)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"replay {rep}"
+
+
+def _random_decode_cases(count=60):
+    rng = np.random.Generator(np.random.PCG64(1202))
+    for c in range(count):
+        n_rows = int(rng.integers(1, 2001))
+        n_cols = int(rng.integers(1, 1501))
+        if rng.random() < 0.5:
+            n_cols = max(8, n_cols - n_cols % 8)          # the aligned path
+        bs = int((32, 64, 128, 256, 512, 1024, 2048, 4096)[rng.integers(0, 8)])
+        m = int(rng.integers(1, 601))
+        transposed = bool(rng.integers(0, 2))
+        ws = ("preferred", "none", "two")[int(rng.integers(0, 3))]
+        yield c, n_rows, n_cols, bs, m, transposed, ws
+
+
+@pytest.mark.parametrize("case", list(_random_decode_cases()), ids=lambda c: f"case{c[0]}")
+def test_random_decode_sweep(case):
+    """A seeded sweep of shapes, block sizes, m (every tile width), both src1
+    orientations and workspace settings: with a selection matrix as src1,
+    dst row i equals the oracle's weight row sel[i] exactly."""
+    c, n_rows, n_cols, bs, m, transposed, ws_kind = case
+    say(f"fused decode sweep case {c}: {n_rows}x{n_cols} bs={bs} m={m} "
+        f"transposed={transposed} workspace={ws_kind}")
+    fmt = "nf4" if c % 2 else "fp4"
+    x = inputs.make_inputs(n_rows * n_cols, bs, fmt, 0.05 - 0.001 * c, seed=5000 + c,
+                           n_rows=n_rows, n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(c))
+    sel = rng.integers(0, n_rows, size=m)
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    ws = {"preferred": None, "none": torch.empty(0, device="cuda"),
+          "two": torch.empty(2 * m * n_cols, device="cuda")}[ws_kind]
+    y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                               blocksize=bs, src1=_src1(b, transposed),
+                               src1_transposed=transposed, workspace=ws).cpu().numpy()
+    bad = np.argwhere(y != w[sel])
+    assert bad.size == 0, f"case {c}: first mismatch at (i, j) = {bad[0]}"
