@@ -14,6 +14,9 @@ Prints ONE JSON line (rank 0, one GPU):
                against MI355X's 8 TB/s HBM peak, and the HBM traffic measured
                by rocprofv3 counters (profiles/), while the built kernel's
                instruction digest matches the one the counters were taken on
+  attainable = the library's memory twin of the kernel (same tiles, loads and
+               stores, no arithmetic) timed on the same buffers: the ceiling
+               of this access pattern on the GPU at hand
   cpu_baseline = the CPU oracle on the same inputs, on the host's threads over
                disjoint element ranges (single_core inside: on one thread)
 Timing protocol after the bitsandbytes issue's evidence plan ("B300 evidence
@@ -795,6 +798,10 @@ def main() -> int:
         dq4.dq4_nested_dequant(**dev, offset=offset, n=n, blocksize=bs, out_dtype=torch.float16,
                                out=out, stream=stream)
 
+    K = args.steps
+    nbatch = max(1, min(args.batches, K))
+    per = [K // nbatch + (1 if i < K % nbatch else 0) for i in range(nbatch)]
+
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -802,9 +809,6 @@ def main() -> int:
 
     # timed region: K steps in `batches` batches, one event pair per batch on
     # the launch stream, wall clock around the whole region
-    K = args.steps
-    nbatch = max(1, min(args.batches, K))
-    per = [K // nbatch + (1 if i < K % nbatch else 0) for i in range(nbatch)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(nbatch)]
     torch.cuda.synchronize()
@@ -825,6 +829,33 @@ def main() -> int:
     achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
     print(f"[bench] {K} timed steps: {ms_per_step * 1e3:.2f} us/step wall, "
           f"{kernel_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
+
+    # the memory twin, after the timed region (whose last output is kept for
+    # the parity check first): the same tiles, loads and stores with no
+    # arithmetic, on the same buffer sets -- the ceiling of this access
+    # pattern on this GPU
+    last_out = sets[(K - 1) % len(sets)][1].cpu()
+    twin_bytes = (n + 1) // 2 + 2 * n
+
+    def twin(k):
+        dev, out = sets[k % len(sets)]
+        dq4.dq4_memory_twin_f16(dev["packed"], n, out=out, stream=stream)
+
+    for k in range(args.warmup):
+        twin(k)
+    torch.cuda.synchronize()
+    tevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nbatch)]
+    k = 0
+    for (e0, e1), m in zip(tevs, per):
+        e0.record(stream)
+        for _ in range(m):
+            twin(k)
+            k += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    twin_us = sum(e0.elapsed_time(e1) * 1e3 for e0, e1 in tevs) / K
+    print(f"[bench] memory twin: {twin_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
 
     traffic = measured_traffic()
     result = {
@@ -853,6 +884,13 @@ def main() -> int:
                       "p10": round(percentile(batch_us, 0.1), 3),
                       "p90": round(percentile(batch_us, 0.9), 3)},
         "kernel_isa_sha256_16": kernel_digest(),
+        "attainable": {"kernel": "dq4_memory_twin_kernel: the same tiles, tile order, loads and "
+                                 "stores, no arithmetic and no metadata",
+                       "us": round(twin_us, 3), "bytes_per_launch": twin_bytes,
+                       "GBps": round(twin_bytes / (twin_us * 1e-6) / 1e9, 2),
+                       "frac_of_peak": round(twin_bytes / (twin_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                             4),
+                       "dequant_over_twin_time": round(kernel_us / twin_us, 4)},
         "device": torch.cuda.get_device_name(0), "env": run_env(torch),
         "cpu_baseline": None,
         "parity": None,
@@ -863,7 +901,7 @@ def main() -> int:
 
         import oracle
 
-        got = sets[(K - 1) % len(sets)][1].cpu().view(torch.int16).numpy().view(np.uint16)
+        got = last_out.view(torch.int16).numpy().view(np.uint16)
 
         def oracle_pass(threads):
             """One oracle pass over the whole tensor, split into `threads`

@@ -22,6 +22,8 @@ cannot be loaded, every call raises.
     dq4_dequant_linear(..., n_out, n_in, blocksize, x, op) -> tensor
                                                    (Y = X W^T or G W, FP16/BF16 GEMM)
     dq4_int8_prep(A, CB, SCB, cols) -> (subA, subB)  (LLM.int8 correction operands)
+    dq4_memory_twin_f16(packed, n) -> tensor       (diagnostic: the FP16 call's memory
+                                                   traffic without its arithmetic)
 """
 from __future__ import annotations
 
@@ -64,6 +66,8 @@ def library() -> ctypes.CDLL:
     lib.dq4_nested_dequant_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i64, i64, i32, i32,
                                             i32, P, P]
     lib.dq4_nested_dequant_rows.restype = i32
+    lib.dq4_memory_twin_f16.argtypes = [P, i64, P, P]
+    lib.dq4_memory_twin_f16.restype = i32
     lib.dq4_rows_per_block.argtypes = [i64, i64, i64]
     lib.dq4_rows_per_block.restype = i64
     lib.dq4_nested_dequant_unfused.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32, P, P, P]
@@ -471,6 +475,23 @@ def dq4_int8_prep(A, CB, SCB, cols, subA=None, subB=None, stream=None):
                                      _stream_handle(device, stream))
     _raise_for(st, "dq4_int8_prep")
     return subA, subB
+
+
+def dq4_memory_twin_f16(packed, n: int, out=None, stream=None):
+    """Diagnostic: the FP16 call's memory traffic without its arithmetic (see
+    include/dq4.h).  `out` (or the returned tensor) holds 2n bytes as n
+    float16 slots; as uint32, out[4u + i] = packed word u."""
+    torch = _torch()
+    if packed.device.type != "cuda" or packed.dtype != torch.uint8 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous uint8 GPU tensor")
+    if packed.numel() < -(-int(n) // 2):
+        raise ValueError(f"packed holds {packed.numel()} bytes, needs {-(-int(n) // 2)}")
+    out = _prepare_out(out, max(int(n), 0), torch.float16, packed.device)
+    with torch.cuda.device(packed.device):
+        st = library().dq4_memory_twin_f16(packed.data_ptr(), int(n), out.data_ptr(),
+                                           _stream_handle(packed.device, stream))
+    _raise_for(st, "dq4_memory_twin_f16")
+    return out
 
 
 def to_device(x, device="cuda"):

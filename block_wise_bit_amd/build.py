@@ -87,8 +87,12 @@ def kernel_bodies(asm: str) -> dict:
 
 def kernel_digests(asm: str) -> dict:
     """{kernel symbol: sha256[:16] of its instructions}: identifies the exact
-    code a measurement was taken on, independent of source-level edits."""
-    return {k: hashlib.sha256(v.encode()).hexdigest()[:16] for k, v in kernel_bodies(asm).items()}
+    code a measurement was taken on, independent of source-level edits.
+    Branch labels are numbered per function in file order (.LBB<f>_<n>); the
+    function number is dropped so that adding a kernel elsewhere in a file
+    leaves the digests of unchanged kernels as they are."""
+    return {k: hashlib.sha256(re.sub(r"\.LBB\d+_(\d+)", r".LBB_\1", v).encode()).hexdigest()[:16]
+            for k, v in kernel_bodies(asm).items()}
 
 
 if __name__ == "__main__":

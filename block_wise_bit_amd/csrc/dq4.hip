@@ -216,6 +216,36 @@ __global__ __launch_bounds__(kThreads) void dq4_elem_kernel(Args a)
         one_element<OUT>(a, lds_scb, lds_cb4, j);
 }
 
+// Memory twin of dq4_tile_kernel<F16> at block size 64: the same 4096-element
+// tiles, tile order, non-temporal packed loads and nt sc1 output stores, with
+// the dequantization taken out -- each packed dword is written four times
+// into its 16-byte output unit.  It moves the headline call's packed and
+// output bytes (all but its scale codes, absmax and codebooks) in the same
+// pattern, so its time is the ceiling that access pattern reaches on the
+// machine it runs on.  A diagnostic: nothing of the method runs here.
+__global__ __launch_bounds__(kThreads) void dq4_memory_twin_kernel(const uint32_t *words,
+                                                                   void *out, int64_t n_tiles)
+{
+    constexpr int kUnits = kDwordsPerLane;  // FP16 units: one packed dword each
+    const int t = threadIdx.x;
+    const int64_t n_paired = n_tiles & ~((int64_t{kXcds} << 1) - 1);  // B = 64: 2 tiles/line
+    for (int64_t slot = blockIdx.x; slot < n_tiles; slot += gridDim.x) {
+        const int64_t tile = slot < n_paired ? xcd_paired_tile(slot, 1) : slot;
+        const int64_t u0 = tile * kTileDwords;
+        uint32_t w[kUnits];
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u)
+            w[u] = load_packed<DQ4_F16>(tile_word<DQ4_F16, kUnits>(words + u0, u, t));
+        const __amdgpu_buffer_rsrc_t dst = unit_buffer(out, u0, kUnits * kThreads);
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const uint32_t ul = tile_unit<DQ4_F16, kUnits>(u, t);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[u], w[u], w[u], w[u]}, dst, ul * 16,
+                                                   0, kPolicyNT | kPolicySC1);
+        }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -333,6 +363,8 @@ bool any_null(const void *a, const void *b, const void *c, const void *d, const 
 }  // namespace dq4
 
 using dq4::Args;
+constexpr int kTileElemsPublic = dq4::kTileElems;
+constexpr int kThreadsPublic = dq4::kThreads;
 
 extern "C" {
 
@@ -380,6 +412,28 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
     const Args a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, out,
                  r0 * n_cols, count, offset, log2_block};
     return dq4::launch(a, out_dtype, stream);
+}
+
+dq4_status_t dq4_memory_twin_f16(const uint8_t *packed, int64_t n, void *out, void *stream)
+{
+    if (n < 0 || n % kTileElemsPublic != 0)
+        return DQ4_EINVAL;
+    if (n == 0)
+        return DQ4_OK;
+    if (!packed || !out || reinterpret_cast<uintptr_t>(packed) % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return DQ4_EINVAL;
+    const uint32_t *words = reinterpret_cast<const uint32_t *>(packed);
+    int64_t n_tiles = n / kTileElemsPublic;
+    if (n_tiles > 0x7FFFFFFF)
+        return DQ4_EUNSUPPORTED;
+    void *o = out;
+    void *params[] = {&words, &o, &n_tiles};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(&dq4::dq4_memory_twin_kernel),
+        dim3(static_cast<uint32_t>(n_tiles)), dim3(kThreadsPublic), params, 0,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DQ4_OK : dq4::hip_failed(e);
 }
 
 int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes)

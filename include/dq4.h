@@ -123,6 +123,21 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
 int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes);
 
 /*
+ * Diagnostic, not part of the method: the memory twin of the FP16 whole-tensor
+ * call at block size 64.  It reads the n/2 packed bytes and writes 2n bytes
+ * to `out` in exactly the tiles, tile order, load policy and store policy of
+ * dq4_nested_dequant's vector path, with the dequantization taken out: each
+ * packed dword is written four times into its 16-byte output unit
+ * (out as uint32: out[4u + i] = packed_as_uint32[u], i < 4).  Its time is
+ * the ceiling that the dequantization's access pattern reaches on the GPU at
+ * hand, the reference beside the nominal HBM peak (the pages' evidence plan
+ * asks for effective bandwidth; this gives the attainable one).
+ * Requires n % 4096 == 0, `packed` 4-byte and `out` 16-byte aligned
+ * (DQ4_EINVAL otherwise); n == 0 is a no-op.  One kernel on `stream`.
+ */
+dq4_status_t dq4_memory_twin_f16(const uint8_t *packed, int64_t n, void *out, void *stream);
+
+/*
  * Unfused three-launch form, kept as the comparison baseline of
  * dq4_nested_dequant: the existing sequence of the bitsandbytes issue above
  * (section "Problem") -- (1) scale codes to an FP32 scale buffer,

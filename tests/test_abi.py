@@ -28,7 +28,7 @@ def test_exports_every_declared_function(lib):
                           "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
                           "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear",
                           "dq4_int8_prep", "dq4_out_prod_fused",
-                          "dq4_out_prod_fused_workspace_bytes"}
+                          "dq4_out_prod_fused_workspace_bytes", "dq4_memory_twin_f16"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -228,3 +228,13 @@ def test_product_path_does_not_reach_the_oracle():
                     text = fh.read()
                 assert "import oracle" not in text and "from oracle" not in text, fname
                 assert "dq4o_" not in text and "dq4_oracle" not in text, fname
+
+
+def test_validation_memory_twin(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.dq4_memory_twin_f16(p, 0, p, None) == dq4.DQ4_OK
+    assert lib.dq4_memory_twin_f16(p, -4096, p, None) == dq4.DQ4_EINVAL
+    assert lib.dq4_memory_twin_f16(p, 4095, p, None) == dq4.DQ4_EINVAL     # whole tiles only
+    assert lib.dq4_memory_twin_f16(None, 4096, p, None) == dq4.DQ4_EINVAL
+    assert lib.dq4_memory_twin_f16(p, 4096, ctypes.c_void_p(8), None) == dq4.DQ4_EINVAL
+    assert lib.dq4_memory_twin_f16(ctypes.c_void_p(2), 4096, p, None) == dq4.DQ4_EINVAL

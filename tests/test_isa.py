@@ -44,7 +44,7 @@ def test_kernels_present(asm):
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
                           ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
                           ("out_prod_fused_kernel", 16), ("out_prod_reduce_kernel", 1),
-                          ("out_prod_zero_kernel", 1)):
+                          ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1)):
         assert sum(kernel in n for n in names) == count, kernel
 
 
@@ -54,7 +54,7 @@ def test_no_fused_or_packed_fp_instructions(asm):
         assert not found, f"{name}: {found}"
         if "add_offset" in name or "reduce" in name:
             assert "v_add_f32" in code, name
-        elif "zero_fill" not in name and "zero_kernel" not in name:
+        elif "zero_fill" not in name and "zero_kernel" not in name and "memory_twin" not in name:
             assert "v_mul_f32" in code, name
         if "dq4_tile_kernel" in name or "dq4_elem_kernel" in name or "out_prod_fused" in name:
             assert "v_add_f32" in code, name   # the scale is rebuilt in the fused kernels
@@ -97,11 +97,12 @@ def test_no_scratch(asm):
 def test_tile_kernels_stream_their_memory_traffic(asm):
     """The vector paths write every output unit with a 16-byte buffer store
     marked nt and sc1 (the measured-fastest store policy on MI355X), and no
-    other kind of 16-byte store appears in them.  The packed data is read
+    other kind of 16-byte store appears in them; so does their memory twin.  The packed data is read
     with non-temporal loads for FP16/BF16 output (instantiations 1 and 2) and
     with plain loads for FP32 output (instantiation 0), as measured fastest."""
     for name, code in _kernel_bodies(asm).items():
-        if "dq4_tile_kernel" not in name and "dq4_value_tile_kernel" not in name:
+        if ("dq4_tile_kernel" not in name and "dq4_value_tile_kernel" not in name
+                and "dq4_memory_twin_kernel" not in name):
             continue
         stores = re.findall(r"^\s*(buffer_store_dwordx4|global_store_dwordx4)\b(.*)$", code,
                             re.M)

@@ -338,3 +338,19 @@ def test_bad_arguments_raise_and_write_nothing():
     assert (out.cpu() == 3.0).all()
     y = dq4.dq4_nested_dequant(**dev, offset=0.0, n=0, blocksize=64)
     assert y.numel() == 0
+
+
+# ----------------------------------------------------------------------------
+# the memory twin (a diagnostic with the FP16 call's traffic, no arithmetic)
+# ----------------------------------------------------------------------------
+def test_memory_twin_writes_each_packed_word_four_times():
+    rng = np.random.Generator(np.random.PCG64(31))
+    n = 4096 * 37
+    packed = rng.integers(0, 256, size=n // 2, dtype=np.uint8)
+    y = dq4.dq4_memory_twin_f16(torch.from_numpy(packed).cuda(), n)
+    torch.cuda.synchronize()
+    got = y.cpu().view(torch.int32).numpy().view(np.uint32)
+    want = np.repeat(packed.view(np.uint32), 4)
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        dq4.dq4_memory_twin_f16(torch.from_numpy(packed).cuda(), n - 8)
