@@ -570,6 +570,16 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         # measure the clock ramp after each synchronization, not the kernel
         inner = n_sets * max(1, math.ceil(4000.0 / (est_us * n_sets)))
         samples = graph_time(call, inner)
+        # the memory twin on the same sets where it applies (FP16-sized output,
+        # whole 4096-element tiles): the ceiling of the access pattern at this size
+        twin_us = None
+        if ob == 2 and n % 4096 == 0:
+            def twin(k):
+                dev, out = sets[k % n_sets]
+                dq4.dq4_memory_twin_f16(dev["packed"], n, out=out.view(torch.float16))
+            for k in range(n_sets):
+                twin(k)
+            twin_us = percentile(graph_time(twin, inner), 0.5)
         del sets
         torch.cuda.empty_cache()
         med = percentile(samples, 0.5)
@@ -579,8 +589,10 @@ def configs_bench(args, torch, dq4, inputs) -> int:
                 "algorithmic_bytes": alg, "GBps": round(alg / (med * 1e-6) / 1e9, 1),
                 "frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "ideal_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 3),
-                "buffer_sets": n_sets, "inner": inner}
-        print(f"[configs] {name}: {med:.2f} us, {cell['GBps']} GB/s ({cell['frac']:.3f})",
+                "buffer_sets": n_sets, "inner": inner,
+                "memory_twin_us": None if twin_us is None else round(twin_us, 3)}
+        print(f"[configs] {name}: {med:.2f} us, {cell['GBps']} GB/s ({cell['frac']:.3f})"
+              + ("" if twin_us is None else f", memory twin {twin_us:.2f} us"),
               file=sys.stderr, flush=True)
         return cell
 
