@@ -27,8 +27,9 @@
 //    leave two waves per SIMD); a ragged m pays for the padded rows of its
 //    last tile, so the width comes from a cost rule (tile_cost);
 //  * per stage of 16 weight rows every lane decodes 8 consecutive weight
-//    elements (one packed dword when n_cols % 8 == 0) with their one or two
-//    block scales, and stages the tile's src1 values;
+//    elements (one packed dword when n_cols % 8 == 0, and then one block
+//    scale, since the 8 elements share a block; else one or two scales),
+//    and stages the tile's src1 values;
 //  * two LDS buffers: the waves decode the next stage into one while the
 //    MFMAs read the other, and the global loads of the stage after that are
 //    issued before the barrier, so each stage costs one barrier and its
