@@ -39,9 +39,11 @@
 //    on one XCD so that the line is fetched from HBM once (workgroups go to
 //    the 8 XCDs in turn, and each XCD has its own L2).  FP32 output measured
 //    faster with plain loads in dispatch order (kStreamPolicy);
-//  * the partial last tile, and any window that does not meet the alignment
-//    of the vector path, go through a per-element path that computes the same
-//    bits.
+//  * the partial last tile goes through a per-element path that computes the
+//    same bits; windows that miss the alignment of this path take a general
+//    vector path (dq4_shift_tile_kernel, output-aligned tiles with
+//    funnel-shifted packed words), and only outputs that are not even
+//    element-aligned take the per-element path throughout.
 // No scratch memory: nothing but the inputs and the output touches HBM.
 
 #include <hip/hip_runtime.h>
@@ -64,6 +66,7 @@ constexpr int kTileDwords = kThreads * kDwordsPerLane;
 constexpr int kTileElems = kTileDwords * 8;    // 4096
 constexpr int kMaxTileBlocks = kTileElems / 32 + 1;  // blocksize 32, tile not block-aligned
 constexpr int kElemBlocksPerCU = 8;            // grid of the per-element path
+constexpr int kOutAlign = 128;    // output alignment of the vector tiles (bytes)
 constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kLog2MaxShare = 3;  // pair up at most 8 tiles per line of scale codes
 
@@ -120,7 +123,8 @@ __device__ __forceinline__ int64_t xcd_paired_tile(int64_t slot, int s)
 }
 
 // Vector path.  Requires e0 % 8 == 0, packed + e0/2 4-byte aligned and out
-// 16-byte aligned.  Tiles [0, n_full) are full; tile n_full (if any) is the
+// 16-byte aligned (the launcher sends it 128-byte aligned outputs only, see
+// kOutAlign).  Tiles [0, n_full) are full; tile n_full (if any) is the
 // partial last tile.  Normally gridDim.x == n_tiles and each workgroup runs
 // one tile; the loop only matters for grids capped below the tile count.
 template <int OUT>
@@ -197,6 +201,135 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[e] = lds_cb4[(static_cast<uint32_t>(w[u]) >> (4 * e)) & 0xFu] * s;
+            store_unit<OUT>(dst, ul, v);
+        }
+        __syncthreads();  // LDS is rewritten by the next tile of this workgroup
+    }
+}
+
+// General vector path, for windows that miss the alignment of dq4_tile_kernel
+// (start element, packed or output pointer) but whose output is
+// element-aligned.  Tiles are aligned to the output instead of the packed
+// bytes: the first `head` outputs (up to the first 128-byte boundary of
+// `out`; stores that start mid-line run ~40 % slower on MI355X) and the last
+// partial tile are computed element by element by the workgroup of slot 0,
+// so that their latency overlaps the full tiles; every full tile of 4096
+// outputs after the head is a dq4_tile_kernel tile whose units take their
+// nibbles from two neighbouring packed dwords, funnel-shifted by a bit
+// offset that is the same for the whole window (one dword when that offset
+// is 0), and whose elements pick one of two block scales, since a unit may
+// straddle two outer blocks.  The packed bytes are read through a buffer
+// resource that ends at the last dword holding a needed nibble: reads past
+// it return zero.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_t head,
+                                                                  int64_t n_full,
+                                                                  int64_t n_tiles)
+{
+    __shared__ float lds_scb[256];
+    __shared__ float lds_cb4[16];
+    __shared__ float lds_scale[kMaxTileBlocks];
+
+    const int t = threadIdx.x;
+    const int lb = a.log2_block;
+    constexpr int E = Unit<OUT>::kElems;
+    constexpr int kUnits = kDwordsPerLane * 8 / E;  // units per lane and tile
+    constexpr int kOutBytes = OUT == DQ4_F32 ? 4 : 2;
+    // plain loads: marking these buffer loads non-temporal measured ~14 %
+    // slower here (the neighbouring dword each unit also reads is then
+    // fetched again rather than found in cache)
+    constexpr int kLoadPolicy = 0;
+
+    // packed bits from a 4-byte aligned base: element g's nibble starts at
+    // bit base_bits + 4 g
+    const uintptr_t p_addr = reinterpret_cast<uintptr_t>(a.packed);
+    const uint8_t *pb = a.packed - (p_addr & 3);
+    const int64_t base_bits = static_cast<int64_t>(p_addr & 3) * 8;
+    const int64_t last_byte = (a.e0 + a.count - 1) >> 1;  // of the needed packed bytes
+    const int64_t span = (p_addr & 3) + last_byte + 1;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(pb), 0, static_cast<int32_t>((span + 3) & ~int64_t{3}),
+        kRawBufferWord3);
+    // the first slot takes the head and the tail when there are any
+    const int64_t edge = n_tiles - n_full;  // 1 or 0
+
+    // FP16/BF16: tiles that read the same 128-byte line of scale codes run on
+    // one XCD, as in dq4_tile_kernel
+    const int log2_share = min(lb - 5, kLog2MaxShare);
+    const int64_t n_paired =
+        kStreamPolicy<OUT> ? n_full & ~((int64_t{kXcds} << log2_share) - 1) : 0;
+    for (int64_t slot = blockIdx.x; slot < n_tiles; slot += gridDim.x) {
+        if (slot < edge) {
+            load_tables(a, lds_scb, lds_cb4);
+            for (int64_t j = t; j < head; j += kThreads)
+                one_element<OUT>(a, lds_scb, lds_cb4, j);
+            for (int64_t j = head + n_full * kTileElems + t; j < a.count; j += kThreads)
+                one_element<OUT>(a, lds_scb, lds_cb4, j);
+            __syncthreads();
+            continue;
+        }
+        const int64_t fs = slot - edge;  // full-tile slot
+        const int64_t tile = fs < n_paired ? xcd_paired_tile(fs, log2_share) : fs;
+
+        // 1. packed words: unit ul covers global elements g .. g + E - 1,
+        //    g = e_tile + ul * E, i.e. bits [4 g, 4 g + 4 E) after the base
+        const int64_t e_tile = a.e0 + head + tile * kTileElems;
+        const int64_t bit0 = base_bits + 4 * e_tile;
+        const uint32_t sh = static_cast<uint32_t>(bit0 & 31);  // the same for every unit
+        uint32_t lo[kUnits], hi[kUnits];
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int64_t bit = bit0 + int64_t{4 * E} * tile_unit<OUT, kUnits>(u, t);
+            const int32_t byte = static_cast<int32_t>((bit >> 5) << 2);
+            lo[u] = __builtin_amdgcn_raw_buffer_load_b32(src, byte, 0, kLoadPolicy);
+            // with sh == 0 every unit's nibbles lie in its first dword
+            hi[u] = sh != 0 ? __builtin_amdgcn_raw_buffer_load_b32(src, byte + 4, 0, kLoadPolicy)
+                            : 0u;
+        }
+
+        // 2. metadata of the outer blocks this tile touches, one block per lane
+        const int64_t b0 = e_tile >> lb;
+        const uint32_t r = static_cast<uint32_t>(e_tile - (b0 << lb));  // offset in block b0
+        const int n_blocks = static_cast<int>((r + kTileElems - 1) >> lb) + 1;
+        const bool has0 = t < n_blocks;
+        const bool has1 = t + kThreads < n_blocks;
+        uint32_t code0 = 0, code1 = 0;
+        float absmax0 = 0.0f, absmax1 = 0.0f;
+        if (has0) {
+            code0 = a.scale_codes[b0 + t];
+            absmax0 = a.nested_absmax[(b0 + t) >> kNestedLog2];
+        }
+        if (has1) {
+            code1 = a.scale_codes[b0 + t + kThreads];
+            absmax1 = a.nested_absmax[(b0 + t + kThreads) >> kNestedLog2];
+        }
+
+        // 3. codebooks to LDS, then every block's scale to LDS
+        load_tables(a, lds_scb, lds_cb4);
+        if (has0)
+            lds_scale[t] = block_scale(lds_scb[code0], absmax0, a.offset);
+        if (has1)
+            lds_scale[t + kThreads] = block_scale(lds_scb[code1], absmax1, a.offset);
+        __syncthreads();
+
+        // 4. value pass: the unit's nibbles funnel-shifted out of (hi, lo);
+        //    element e of the unit is in the unit's first block or the next
+        void *out_tile = static_cast<char *>(a.out) + (head + tile * kTileElems) * kOutBytes;
+        const __amdgpu_buffer_rsrc_t dst = unit_buffer(out_tile, 0, kUnits * kThreads);
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const uint32_t ul = tile_unit<OUT, kUnits>(u, t);
+            const uint32_t ush = (sh + 4 * E * ul) & 31;  // FP32 units start mid-dword
+            const uint32_t word = __builtin_amdgcn_alignbit(hi[u], lo[u], ush);
+            const uint32_t first = r + ul * E;             // offset from block b0's start
+            const float s_lo = lds_scale[first >> lb];
+            const float s_hi = lds_scale[(first + E - 1) >> lb];
+            float v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float s = ((first + e) >> lb) == (first >> lb) ? s_lo : s_hi;
+                v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * s;
+            }
             store_unit<OUT>(dst, ul, v);
         }
         __syncthreads();  // LDS is rewritten by the next tile of this workgroup
@@ -309,20 +442,47 @@ int32_t last_hip_error()
 }
 
 namespace {
+// The shifted vector path needs an element-aligned output, at least one full
+// tile after the head, and packed bytes that a buffer resource can span
+// (offsets below 2^31).
+bool shift_path_fits(const Args &a, int64_t out_bytes)
+{
+    if (reinterpret_cast<uintptr_t>(a.out) % out_bytes != 0)
+        return false;
+    if (a.count < kTileElems + kOutAlign)
+        return false;
+    const int64_t span = static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.packed) & 3) +
+                         ((a.e0 + a.count - 1) >> 1) + 1;
+    return span + 8 < (int64_t{1} << 31);
+}
+
 template <int OUT>
 dq4_status_t launch_typed(const Args &a, hipStream_t stream)
 {
     Args args = a;
     hipError_t e;
+    // dq4_tile_kernel: aligned start, packed dwords and a 128-byte aligned
+    // output (16-byte aligned stores that start mid-line run ~40 % slower)
     const bool vec = (a.e0 % 8 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.packed + (a.e0 >> 1)) % 4 == 0) &&
-                     (reinterpret_cast<uintptr_t>(a.out) % 16 == 0);
+                     (reinterpret_cast<uintptr_t>(a.out) % kOutAlign == 0);
     if (vec) {
         int64_t n_full = a.count / kTileElems;
         int64_t n_tiles = (a.count + kTileElems - 1) / kTileElems;
         const int64_t grid = n_tiles < kMaxGrid ? n_tiles : kMaxGrid;
         void *params[] = {&args, &n_full, &n_tiles};
         e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4_tile_kernel<OUT>),
+                            dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, stream);
+    } else if (shift_path_fits(a, OUT == DQ4_F32 ? 4 : 2)) {
+        const int64_t out_bytes = OUT == DQ4_F32 ? 4 : 2;
+        int64_t head = ((kOutAlign - static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.out) %
+                                                           kOutAlign)) % kOutAlign) / out_bytes;
+        int64_t n_full = (a.count - head) / kTileElems;
+        const bool edge = head > 0 || head + n_full * kTileElems < a.count;
+        int64_t n_tiles = n_full + (edge ? 1 : 0);  // slot 0 takes head and tail
+        const int64_t grid = n_tiles < kMaxGrid ? n_tiles : kMaxGrid;
+        void *params[] = {&args, &head, &n_full, &n_tiles};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT>),
                             dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, stream);
     } else {
         int device = 0;

@@ -44,7 +44,8 @@ def test_kernels_present(asm):
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
                           ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
                           ("out_prod_fused_kernel", 16), ("out_prod_reduce_kernel", 1),
-                          ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1)):
+                          ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1),
+                          ("dq4_shift_tile_kernel", 3)):
         assert sum(kernel in n for n in names) == count, kernel
 
 

@@ -354,3 +354,53 @@ def test_memory_twin_writes_each_packed_word_four_times():
     assert np.array_equal(got, want)
     with pytest.raises(ValueError):
         dq4.dq4_memory_twin_f16(torch.from_numpy(packed).cuda(), n - 8)
+
+
+# ----------------------------------------------------------------------------
+# the shifted vector path: element-aligned but otherwise misaligned windows
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("bs", [32, 64, 4096])
+@pytest.mark.parametrize("out_shift,packed_shift", [(1, 0), (0, 1), (3, 2), (5, 3)])
+def test_shifted_vector_path(dt, bs, out_shift, packed_shift):
+    """Outputs shifted by out_shift elements and packed bytes by packed_shift
+    bytes from their natural alignment, over 5 full tiles plus a head and a
+    tail: the funnel-shifted units and two-scale elements give the oracle's
+    bits."""
+    n = 5 * 4096 + 1000 + 3
+    x = inputs.make_inputs(n, bs, "nf4", -0.05, seed=77 + bs + out_shift)
+    dev = dq4.to_device(x)
+    if packed_shift:
+        holder = torch.zeros(x.packed.size + packed_shift, dtype=torch.uint8, device="cuda")
+        holder[packed_shift:] = dev["packed"]
+        dev["packed"] = holder[packed_shift:]
+    tdt = torch_dtype(dt)
+    backing = torch.full((n + out_shift + 8,), float("nan"), dtype=tdt, device="cuda")
+    out = backing[out_shift:out_shift + n]
+    dq4.dq4_nested_dequant(**dev, offset=float(x.offset), n=n, blocksize=bs, out_dtype=tdt,
+                           out=out)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(out), oracle_bits(x, dt), f"shifted {dt} bs={bs}")
+    assert torch.isnan(backing[:out_shift].float()).all()
+    assert torch.isnan(backing[out_shift + n:].float()).all()
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_odd_width_row_windows_full_size(dt):
+    """A 28672 x 8191 weight (odd width: windows start mid-byte) in windows of
+    4001 rows, every window against the oracle's rows."""
+    n_rows, n_cols = 28672, 8191
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=8191, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    tdt = torch_dtype(dt)
+    buf = torch.empty(4001 * n_cols, dtype=tdt, device="cuda")
+    for r0 in range(0, n_rows, 4001):
+        rows = min(4001, n_rows - r0)
+        say(f"odd-width window r0={r0} rows={rows} {dt}")
+        y = dq4.dq4_nested_dequant_rows(**dev, offset=float(x.offset), n_rows=n_rows,
+                                        n_cols=n_cols, r0=r0, rows=rows, blocksize=64,
+                                        out_dtype=tdt, out=buf)
+        got = bits_of(y[: rows * n_cols])
+        want = oracle_bits(x, dt, first=r0 * n_cols, count=rows * n_cols)
+        assert_bits_equal(got, want, f"odd-width window r0={r0}")
