@@ -100,7 +100,10 @@ def test_output_is_not_written_past_n():
                 assert (out[n:].cpu() == 7.0).all(), f"wrote past n={n} ({dt}, shift={shift})"
 
 
-def test_unaligned_pointers_use_the_element_path_with_same_bits():
+def test_unaligned_pointers_give_the_same_bits():
+    """Packed bytes and output one byte / one element off their alignment: the
+    general vector path (funnel-shifted packed words, output-aligned tiles)
+    gives the oracle's bits."""
     n = 100_003
     x = inputs.make_inputs(n, 64, "nf4", 0.03, seed=77)
     want = oracle_bits(x, "f16")
