@@ -543,13 +543,16 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         del g
         return samples
 
-    def whole_cell(name, x, dt_name):
+    def whole_cell(name, x, dt_name, out_shift=0):
         tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt_name]
         ob = 4 if dt_name == "f32" else 2
         n, bs = x.n, x.blocksize
         alg = algorithmic_bytes(n, bs, ob)
         n_sets = max(2, math.ceil(COLD_PACKED_BYTES / ((n + 1) // 2)))
-        sets = [(dq4.to_device(x, "cuda:0"), torch.empty(n, dtype=tdt, device="cuda:0"))
+        # out_shift > 0: the output starts out_shift elements into its buffer,
+        # off the 128-byte alignment of the fast path (the general vector path)
+        sets = [(dq4.to_device(x, "cuda:0"),
+                 torch.empty(n + out_shift, dtype=tdt, device="cuda:0")[out_shift:])
                 for _ in range(n_sets)]
 
         def call(k):
@@ -573,7 +576,7 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         # the memory twin on the same sets where it applies (FP16-sized output,
         # whole 4096-element tiles): the ceiling of the access pattern at this size
         twin_us = None
-        if ob == 2 and n % 4096 == 0:
+        if ob == 2 and n % 4096 == 0 and out_shift == 0:
             def twin(k):
                 dev, out = sets[k % n_sets]
                 dq4.dq4_memory_twin_f16(dev["packed"], n, out=out.view(torch.float16))
@@ -584,6 +587,7 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         torch.cuda.empty_cache()
         med = percentile(samples, 0.5)
         cell = {"workload": name, "n": n, "blocksize": bs, "format": x.fmt, "out": dt_name,
+                "out_shift_elements": out_shift,
                 "offset": float(x.offset), "us": round(med, 3),
                 "p10_p90": [round(percentile(samples, q), 3) for q in (0.1, 0.9)],
                 "algorithmic_bytes": alg, "GBps": round(alg / (med * 1e-6) / 1e9, 1),
@@ -602,7 +606,11 @@ def configs_bench(args, torch, dq4, inputs) -> int:
     for wl in inputs.mid_matrix_workloads():
         cells.append(whole_cell(wl.name, wl.inputs(), wl.out_dtype))
     wl = inputs.HEADLINE
-    cells.append(whole_cell(wl.name, wl.inputs(), wl.out_dtype))
+    x = wl.inputs()
+    cells.append(whole_cell(wl.name, x, wl.out_dtype))
+    for shift in (1, 8):   # the general vector path: misaligned output
+        cells.append(whole_cell(f"{wl.name}_out+{shift}", x, wl.out_dtype, out_shift=shift))
+    del x
     for bs in inputs.TAIL_SWEEP_BLOCKSIZES:
         for fmt in ("nf4", "fp4"):
             x = inputs.make_inputs(inputs.TAIL_SWEEP_N, bs, fmt, 0.1, seed=inputs.SEED_BASE + 4)
