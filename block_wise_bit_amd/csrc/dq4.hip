@@ -125,7 +125,7 @@ __device__ __forceinline__ int64_t xcd_paired_tile(int64_t slot, int s)
 // Vector path.  Requires e0 % 8 == 0, packed + e0/2 4-byte aligned and out
 // 16-byte aligned (the launcher sends it 128-byte aligned outputs only, see
 // kOutAlign).  Tiles [0, n_full) are full; tile n_full (if any) is the
-// partial last tile.  Normally gridDim.x == n_tiles and each workgroup runs
+// partial last tile, run by slot 0.  Normally gridDim.x == n_tiles and each workgroup runs
 // one tile; the loop only matters for grids capped below the tile count.
 template <int OUT>
 __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_full,
@@ -143,16 +143,20 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
     const int log2_share = min(lb - 5, kLog2MaxShare);  // tiles per line of codes
     const int64_t n_paired =
         kStreamPolicy<OUT> ? n_full & ~((int64_t{kXcds} << log2_share) - 1) : 0;
+    // the partial tile, if any, goes to the first slot: dispatched last, its
+    // per-element work would add to the end of the launch
+    const int64_t edge = n_tiles - n_full;  // 1 or 0
     for (int64_t slot = blockIdx.x; slot < n_tiles; slot += gridDim.x) {
-        const int64_t tile = slot < n_paired ? xcd_paired_tile(slot, log2_share) : slot;
-        const int64_t d0 = tile * kTileDwords;  // first packed dword of the tile
-        if (tile >= n_full) {
+        if (slot < edge) {
             load_tables(a, lds_scb, lds_cb4);
-            for (int64_t j = d0 * 8 + t; j < a.count; j += kThreads)
+            for (int64_t j = n_full * kTileElems + t; j < a.count; j += kThreads)
                 one_element<OUT>(a, lds_scb, lds_cb4, j);
             __syncthreads();
             continue;
         }
+        const int64_t fs = slot - edge;  // full-tile slot
+        const int64_t tile = fs < n_paired ? xcd_paired_tile(fs, log2_share) : fs;
+        const int64_t d0 = tile * kTileDwords;  // first packed dword of the tile
 
         // 1. packed data first: the longest-latency loads
         using Word = typename Unit<OUT>::Word;

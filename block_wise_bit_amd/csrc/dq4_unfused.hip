@@ -69,9 +69,12 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
     __shared__ float lds_scale[kMaxTileBlocks];
     const int t = threadIdx.x;
 
-    for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        if (tile != blockIdx.x)
+    const int64_t edge = n_tiles - n_full;  // 1 or 0
+    for (int64_t slot = blockIdx.x; slot < n_tiles; slot += gridDim.x) {
+        if (slot != blockIdx.x)
             __syncthreads();  // LDS still holds the previous tile of this workgroup
+        // the partial tile, if any, goes to the first slot, as in the fused kernel
+        const int64_t tile = slot < edge ? n_full : slot - edge;
         const int64_t d0 = tile * kTileDwords;
         const float cv = t < 16 ? codebook4[t] : 0.0f;
         if (tile >= n_full) {
