@@ -542,7 +542,7 @@ dq4_status_t dq4_nested_dequant(const uint8_t *packed, const uint8_t *scale_code
     const dq4_status_t st = dq4::validate_layout(blocksize, nested_blocksize, out_dtype, &log2_block);
     if (st != DQ4_OK)
         return st;
-    if (n < 0)
+    if (n < 0 || n > dq4::kMaxElems)
         return DQ4_EINVAL;
     if (n == 0)
         return DQ4_OK;
@@ -566,7 +566,7 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
         return st;
     if (n_rows < 0 || n_cols < 0 || r0 < 0 || rows < 0 || r0 > n_rows || rows > n_rows - r0)
         return DQ4_EINVAL;
-    if (n_cols != 0 && n_rows > INT64_MAX / n_cols)
+    if (n_cols != 0 && n_rows > dq4::kMaxElems / n_cols)
         return DQ4_EINVAL;
     const int64_t count = rows * n_cols;
     if (count == 0)

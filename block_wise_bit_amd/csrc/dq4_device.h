@@ -19,6 +19,9 @@
 namespace dq4 {
 
 constexpr int kNestedLog2 = 8;  // 256 outer blocks per nested absmax
+// Largest element count an entry point accepts: far beyond any device's
+// memory, and small enough that index and tile arithmetic stays in int64.
+constexpr int64_t kMaxElems = int64_t{1} << 62;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

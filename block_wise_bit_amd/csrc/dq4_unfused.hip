@@ -176,7 +176,7 @@ extern "C" {
 
 int64_t dq4_unfused_workspace_bytes(int64_t n, int32_t blocksize)
 {
-    if (n <= 0 || blocksize <= 0)
+    if (n <= 0 || n > dq4::kMaxElems || blocksize <= 0)
         return 0;
     return ((n + blocksize - 1) / blocksize) * static_cast<int64_t>(sizeof(float));
 }
@@ -193,7 +193,7 @@ dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *sc
         dq4::validate_layout(blocksize, nested_blocksize, out_dtype, &log2_block);
     if (st != DQ4_OK)
         return st;
-    if (n < 0)
+    if (n < 0 || n > dq4::kMaxElems)
         return DQ4_EINVAL;
     if (n == 0)
         return DQ4_OK;

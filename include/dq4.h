@@ -62,8 +62,9 @@ typedef int32_t dq4_status_t;
 
 enum {
     DQ4_OK = 0,
-    DQ4_EINVAL = 1,        /* null pointer with work to do, negative size, bad
-                              row window, unknown output type */
+    DQ4_EINVAL = 1,        /* null pointer with work to do, negative size or
+                              more than 2^62 elements, bad row window,
+                              unknown output type */
     DQ4_EUNSUPPORTED = 2,  /* blocksize not a power of two in [32, 4096], or
                               nested_blocksize other than 256 */
     DQ4_EHIP = 3,          /* the kernel launch failed */
@@ -162,7 +163,7 @@ dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *sc
                                         float *scale_workspace, void *out, void *stream);
 
 /* Bytes of FP32 scale workspace dq4_nested_dequant_unfused needs: 4 * ceil(n /
- * blocksize); 0 for non-positive arguments.  Host only. */
+ * blocksize); 0 for non-positive arguments or n above 2^62.  Host only. */
 int64_t dq4_unfused_workspace_bytes(int64_t n, int32_t blocksize);
 
 /*

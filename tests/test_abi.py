@@ -56,6 +56,8 @@ def test_validation_whole_tensor(lib):
     assert _call(lib, n=0) == dq4.DQ4_OK                          # no-op
     assert _call(lib, n=0, ptr=0, out=0) == dq4.DQ4_OK            # no-op, null pointers allowed
     assert _call(lib, n=-1) == dq4.DQ4_EINVAL
+    assert _call(lib, n=(1 << 62) + 1) == dq4.DQ4_EINVAL         # beyond any tensor
+    assert _call(lib, n=(1 << 63) - 1) == dq4.DQ4_EINVAL
     assert _call(lib, ptr=0) == dq4.DQ4_EINVAL
     assert _call(lib, out=0) == dq4.DQ4_EINVAL
     assert _call(lib, dtype=3) == dq4.DQ4_EINVAL
@@ -74,6 +76,7 @@ def test_validation_unfused(lib):
                                               nested, dtype, ws, p, None)
     assert call(n=0) == dq4.DQ4_OK
     assert call(n=-5) == dq4.DQ4_EINVAL
+    assert call(n=(1 << 63) - 1) == dq4.DQ4_EINVAL
     assert call(ws=None) == dq4.DQ4_EINVAL
     assert call(blocksize=100) == dq4.DQ4_EUNSUPPORTED
     assert call(nested=64) == dq4.DQ4_EUNSUPPORTED
@@ -82,6 +85,7 @@ def test_validation_unfused(lib):
     assert dq4.dq4_unfused_workspace_bytes(1024, 64) == 4 * 16
     assert dq4.dq4_unfused_workspace_bytes(1025, 64) == 4 * 17
     assert dq4.dq4_unfused_workspace_bytes(0, 64) == 0
+    assert dq4.dq4_unfused_workspace_bytes((1 << 63) - 1, 64) == 0   # no overflow
 
 
 def test_validation_out_prod(lib):
@@ -185,6 +189,7 @@ def test_validation_rows(lib):
     assert _call_rows(lib, r0=11, rows=0) == dq4.DQ4_EINVAL
     assert _call_rows(lib, n_rows=-1) == dq4.DQ4_EINVAL
     assert _call_rows(lib, n_rows=1 << 40, n_cols=1 << 40) == dq4.DQ4_EINVAL   # overflow
+    assert _call_rows(lib, n_rows=1 << 31, n_cols=(1 << 31) + 1, rows=0) == dq4.DQ4_EINVAL
     assert _call_rows(lib, ptr=0) == dq4.DQ4_EINVAL
     assert _call_rows(lib, blocksize=24) == dq4.DQ4_EUNSUPPORTED
     assert _call_rows(lib, dtype=7) == dq4.DQ4_EINVAL
