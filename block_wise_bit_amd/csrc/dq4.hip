@@ -222,10 +222,15 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 // nibbles from two neighbouring packed dwords, funnel-shifted by a bit
 // offset that is the same for the whole window (one dword when that offset
 // is 0), and whose elements pick one of two block scales, since a unit may
-// straddle two outer blocks.  The packed bytes are read through a buffer
-// resource that ends at the last dword holding a needed nibble: reads past
-// it return zero.
-template <int OUT>
+// straddle two outer blocks.  kWhole is the instantiation for windows whose
+// units each lie in one packed dword (FP32: half of one) and one block: one
+// load and one scale per unit, as in dq4_tile_kernel.  Compiled separately,
+// it ran an 8-element output shift of the 28672 x 8192 headline shape in
+// 93.8-94.1 us against 98.9-99.1 us through the general instantiation (a
+// runtime branch inside one kernel gained nothing).  The packed bytes are
+// read through a buffer resource that ends at the last dword holding a
+// needed nibble: reads past it return zero.
+template <int OUT, bool kWhole>
 __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_t head,
                                                                   int64_t n_full,
                                                                   int64_t n_tiles)
@@ -287,8 +292,9 @@ __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_
             const int32_t byte = static_cast<int32_t>((bit >> 5) << 2);
             lo[u] = __builtin_amdgcn_raw_buffer_load_b32(src, byte, 0, kLoadPolicy);
             // with sh == 0 every unit's nibbles lie in its first dword
-            hi[u] = sh != 0 ? __builtin_amdgcn_raw_buffer_load_b32(src, byte + 4, 0, kLoadPolicy)
-                            : 0u;
+            hi[u] = !kWhole && sh != 0
+                        ? __builtin_amdgcn_raw_buffer_load_b32(src, byte + 4, 0, kLoadPolicy)
+                        : 0u;
         }
 
         // 2. metadata of the outer blocks this tile touches, one block per lane
@@ -323,16 +329,25 @@ __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const uint32_t ul = tile_unit<OUT, kUnits>(u, t);
-            const uint32_t ush = (sh + 4 * E * ul) & 31;  // FP32 units start mid-dword
-            const uint32_t word = __builtin_amdgcn_alignbit(hi[u], lo[u], ush);
             const uint32_t first = r + ul * E;             // offset from block b0's start
-            const float s_lo = lds_scale[first >> lb];
-            const float s_hi = lds_scale[(first + E - 1) >> lb];
             float v[E];
+            if constexpr (kWhole) {
+                // one dword (FP32: half of one) and one block per unit
+                const uint32_t word = lo[u] >> ((sh + 4 * E * ul) & 31);
+                const float s = lds_scale[first >> lb];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float s = ((first + e) >> lb) == (first >> lb) ? s_lo : s_hi;
-                v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * s;
+                for (int e = 0; e < E; ++e)
+                    v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * s;
+            } else {
+                const uint32_t ush = (sh + 4 * E * ul) & 31;  // FP32 units start mid-dword
+                const uint32_t word = __builtin_amdgcn_alignbit(hi[u], lo[u], ush);
+                const float s_lo = lds_scale[first >> lb];
+                const float s_hi = lds_scale[(first + E - 1) >> lb];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float s = ((first + e) >> lb) == (first >> lb) ? s_lo : s_hi;
+                    v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * s;
+                }
             }
             store_unit<OUT>(dst, ul, v);
         }
@@ -486,8 +501,17 @@ dq4_status_t launch_typed(const Args &a, hipStream_t stream)
         int64_t n_tiles = n_full + (edge ? 1 : 0);  // slot 0 takes head and tail
         const int64_t grid = n_tiles < kMaxGrid ? n_tiles : kMaxGrid;
         void *params[] = {&args, &head, &n_full, &n_tiles};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT>),
-                            dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, stream);
+        // whole units: if the first full tile's units each lie in one packed
+        // dword and one block, every tile's do (tiles are 4096 elements apart)
+        constexpr int E = Unit<OUT>::kElems;
+        const int64_t e_first = a.e0 + head;
+        const int64_t sh =
+            (static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.packed) & 3) * 8 + 4 * e_first) & 31;
+        const bool whole = sh % (4 * E) == 0 && e_first % E == 0;
+        const void *kernel = whole ? reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, true>)
+                                   : reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, false>);
+        e = hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0,
+                            stream);
     } else {
         int device = 0;
         e = hipGetDevice(&device);

@@ -49,8 +49,12 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *p, int64_t count)
         p[i] = 0.0f;
 }
 
-// One rocBLAS handle per (thread, device), created on first use and kept for
-// the life of the thread: rocBLAS handles must not be shared between threads.
+// One rocBLAS handle per (thread, device), created on first use: rocBLAS
+// handles must not be shared between threads.  They are never destroyed; a
+// thread_local destructor can run after the HIP runtime has shut down at
+// process exit, so each thread that calls a GEMM entry point keeps its
+// handles (a few KB of host state and rocBLAS's device workspace per device)
+// until the process ends.
 thread_local std::unordered_map<int, rocblas_handle> t_handles;
 thread_local int32_t t_last_blas_status = 0;
 
