@@ -1,7 +1,8 @@
 """GPU parity over a seeded random sweep of layouts, bit for bit (0 ULP).
 
 The structured tests pin chosen layouts; this sweep draws 240 more from one
-seed: shapes (1..400 rows x 1..3000 columns), every block size 32..4096,
+seed (and 36 from another, all of them layouts of the general vector path's
+whole-unit instantiation): shapes (1..400 rows x 1..3000 columns), every block size 32..4096,
 NF4/FP4, the three output types, offsets of both signs (and exact zero),
 whole-tensor calls and row windows, with the packed bytes and the output
 shifted off their natural alignment in some cases so that both the vector
@@ -53,8 +54,44 @@ def _cases():
         yield (c, n_rows, n_cols, bs, fmt, dt, offset, window, r0, rows, packed_shift, out_shift)
 
 
+def _whole_unit_cases():
+    """Layouts the general vector path's whole-unit instantiation takes: the
+    first full tile's 4-bit codes start on a packed dword (FP32: half of one)
+    and its units inside one block.  n_cols is a multiple of 8, so every row
+    window starts on a multiple of 8 elements; the output is 16 bytes (or, for
+    FP32, 16 or 32 bytes) past a 128-byte line and the packed bytes 0 or 4
+    bytes past a line."""
+    rng = np.random.Generator(np.random.PCG64(20261203))
+    for c in range(N_WHOLE_CASES):
+        n_cols = 8 * int(rng.integers(8, 376))
+        n_rows = int(rng.integers(-(-9000 // n_cols), 401))
+        bs = int(BLOCKSIZES[rng.integers(0, len(BLOCKSIZES))])
+        fmt = ("nf4", "fp4")[int(rng.integers(0, 2))]
+        dt = ("f16", "bf16", "f32")[int(rng.integers(0, 3))]
+        offset = float(np.float32(rng.uniform(-0.2, 0.2)))
+        window = rng.random() < 0.5
+        rows_min = -(-(4096 + 128) // n_cols)
+        r0 = int(rng.integers(0, n_rows - rows_min + 1)) if window else 0
+        rows = int(rng.integers(rows_min, n_rows - r0 + 1)) if window else n_rows
+        packed_shift = int((0, 4)[rng.integers(0, 2)])
+        out_shift = 8 if dt != "f32" else int((4, 8)[rng.integers(0, 2)])
+        yield (c, n_rows, n_cols, bs, fmt, dt, offset, window, r0, rows, packed_shift, out_shift)
+
+
+N_WHOLE_CASES = 36
+
+
+@pytest.mark.parametrize("case", list(_whole_unit_cases()), ids=lambda c: f"whole{c[0]}")
+def test_random_whole_unit_layout(case):
+    _run_case(case)
+
+
 @pytest.mark.parametrize("case", list(_cases()), ids=lambda c: f"case{c[0]}")
 def test_random_layout(case):
+    _run_case(case)
+
+
+def _run_case(case):
     c, n_rows, n_cols, bs, fmt, dt, offset, window, r0, rows, packed_shift, out_shift = case
     n = n_rows * n_cols
     say(f"case {c}: {n_rows}x{n_cols} bs={bs} {fmt} {dt} offset={offset} "
