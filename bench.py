@@ -42,6 +42,47 @@ KERNEL_DIGESTS = os.path.join(ROOT, "block_wise_bit_amd", "libdq4_kernels.json")
 HEADLINE_KERNEL = "_ZN3dq412_GLOBAL__N_115dq4_tile_kernelILi1EEEvNS0_4ArgsEll"
 
 
+def host_threads() -> int:
+    """Threads for the CPU oracle: the machine's CPU share, whatever os.cpu_count() reports."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_dequant_threaded(x, first: int, count: int, dt_name: str, threads: int):
+    """The C oracle over elements [first, first + count) of the inputs x,
+    split into `threads` disjoint element ranges run concurrently (the oracle
+    releases the GIL while it runs).  Returns (output as the oracle gives it:
+    uint16 bits for FP16/BF16, float32 for FP32; seconds of wall clock)."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle
+
+    out = np.empty(count, dtype=np.float32 if dt_name == "f32" else np.uint16)
+    chunk = -(-count // threads) if count else 1
+    chunk += (-chunk) % 8
+
+    def one(start):
+        c = min(chunk, count - start)
+        out[start:start + c] = oracle.dequant_range(
+            x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook, x.codebook4,
+            x.offset, first + start, c, x.blocksize, x.nested_blocksize, dt_name)
+
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(one, range(0, count, chunk)))
+    return out, time.perf_counter() - t0
+
+
+def device_bits(t):
+    """A device tensor's values as host bits (uint16 for 16-bit types, float32 otherwise)."""
+    import numpy as np
+    import torch
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
 def algorithmic_bytes(n: int, blocksize: int, out_bytes: int, nested: int = 256) -> int:
     """Bytes the method must move once: packed nibbles, codes, absmax, codebooks, output."""
     nb = -(-n // blocksize)
@@ -138,6 +179,8 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
     reads its packed weight from HBM, not from the last-level cache."""
     import math
 
+    import numpy as np
+
     all_dtypes = (("f16", torch.float16, 2), ("bf16", torch.bfloat16, 2),
                   ("f32", torch.float32, 4))
     # the primary matrix, then the odd-tail control (1-D, odd length: a packed
@@ -222,6 +265,18 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
                                                out_dtype=tdt, out=out0, scale_workspace=ws0)
                 iview = torch.int32 if ob == 4 else torch.int16
                 bit_equal = bool(torch.equal(ref.view(iview), out0.view(iview)))
+                oracle_cell = None
+                if not args.no_cpu:
+                    # the oracle beside it: timed over the whole tensor, and the
+                    # fused output compared with it bit for bit
+                    want, t_cpu = oracle_dequant_threaded(x, 0, n, dt, host_threads())
+                    hv = np.uint32 if ob == 4 else np.uint16
+                    oracle_cell = {
+                        "seconds": round(t_cpu, 4), "cores": host_threads(),
+                        "GBps": round(alg / t_cpu / 1e9, 3),
+                        "mismatches": int(np.count_nonzero(device_bits(ref).view(hv)
+                                                           != want.view(hv)))}
+                    del want
                 del ref
                 med = {k: percentile(v, 0.5) for k, v in samples.items()}
                 f_med, u_med = med["fused"], med["unfused"]
@@ -238,7 +293,8 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
                         "eager_unfused_us": round(med["unfused_eager"], 2),
                         "eager_speedup": round(med["unfused_eager"] / med["fused_eager"], 4),
                         "samples_us": {k: [round(x, 2) for x in v] for k, v in samples.items()},
-                        "buffer_sets": n_sets, "inner": inner, "bit_equal": bit_equal}
+                        "buffer_sets": n_sets, "inner": inner, "bit_equal": bit_equal,
+                        "oracle": oracle_cell}
                 cells.append(cell)
                 print(f"[compare] {cell['shape']} {fmt} {dt}: fused {f_med:.2f} us, "
                       f"unfused {u_med:.2f} us, x{u_med / f_med:.3f} (eager "
@@ -256,6 +312,8 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
     eager = [c["eager_speedup"] for c in main if c["out"] in ("f16", "bf16")]
     odd_tail = {c["format"]: c["speedup"] for c in cells if c["control"] == "odd_tail"}
     all_equal = all(c["bit_equal"] for c in cells)
+    if not args.no_cpu:
+        all_equal = all_equal and all(c["oracle"]["mismatches"] == 0 for c in cells)
     print(json.dumps({
         "metric": "fused vs unfused nested dequant speedup, geomean over NF4/FP4 x FP16/BF16, "
                   "bs64, primary standalone matrix",
@@ -266,7 +324,9 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
         "timing": "device time per call from HIP-graph replays of `inner` calls, median of "
                   ">= 7 interleaved batches; eager_* = the same calls launched from Python",
         "min_primary_speedup": round(min(primary), 4),
-        "fused_equals_unfused_bitwise": all_equal,
+        "fused_equals_unfused_bitwise": all(c["bit_equal"] for c in cells),
+        "fused_equals_oracle_bitwise": None if args.no_cpu else
+            all(c["oracle"]["mismatches"] == 0 for c in cells),
         "n_gpus": 1, "warmup": args.warmup, "data": "synthetic", "cells": cells,
         "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
     return 0 if all_equal else 3
@@ -341,6 +401,37 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
     tflops = {name: round(flops / (t * 1e-3) / 1e12, 2)
               for name, t in (("fused", t_fused), ("blocked", t_blocked), ("whole", t_whole))}
     best = max(tflops.values())
+    cpu, sampled = None, None
+    if not args.no_cpu:
+        # the oracle beside it, on a bounded sample: the first row window is a
+        # weight of its own (rows 0 .. rows_pb - 1, the prefix of every array).
+        # The fused route runs on it; the oracle dequantizes it and numpy sums
+        # the products in float64; the fused result must lie within the FP32
+        # summation bound gamma_K * sum |src1| |w| of that float64 sum.
+        import numpy as np
+        rows_s = rows_pb
+        dst_s = torch.empty((m, wl.n_cols), dtype=torch.float32, device="cuda:0")
+        dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=rows_s, n_cols=wl.n_cols,
+                               blocksize=64, src1=src1[:rows_s], dst=dst_s)
+        got_s = dst_s.cpu().numpy().astype(np.float64)
+        a_s = src1[:rows_s].cpu().numpy().astype(np.float64)
+        w_s, t_deq = oracle_dequant_threaded(x, 0, rows_s * wl.n_cols, "f32", host_threads())
+        w_s = w_s.reshape(rows_s, wl.n_cols).astype(np.float64)
+        t0 = time.perf_counter()
+        ref = a_s.T @ w_s
+        t_mm = time.perf_counter() - t0
+        bound = np.abs(a_s).T @ np.abs(w_s)
+        k = float(rows_s) * 2.0 ** -24
+        excess = np.abs(got_s - ref) / np.maximum(k / (1 - k) * bound, 1e-300)
+        sample_flops = 2.0 * m * rows_s * wl.n_cols
+        cpu = {"value": round(sample_flops / (t_deq + t_mm) / 1e12, 5), "unit": "TFLOP/s",
+               "cores": host_threads(), "kind": "oracle",
+               "sample": f"rows 0..{rows_s - 1} of {wl.n_rows} (the first row window), m = {m}: "
+                         f"the C oracle's dequantization on {host_threads()} threads "
+                         f"({t_deq:.2f} s) then numpy's float64 product ({t_mm:.2f} s)"}
+        sampled = {"rows": rows_s, "max_error_over_fp32_bound": round(float(excess.max()), 4),
+                   "within_bound": bool(excess.max() <= 1.0)}
+        del a_s, w_s, ref, bound, got_s, dst_s
     print(json.dumps({
         "metric": "out_prod of the 151936x5376 NF4 output head, FP32 TFLOP/s (fused route)",
         "value": tflops["fused"], "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
@@ -357,9 +448,9 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
         "blocked_vs_whole_max_rel_diff": rel_whole, "fused_vs_blocked_max_rel_diff": rel_fused,
         "roofline": {"bound": "mfma", "achieved": tflops["fused"], "peak": 157.3,
                      "unit": "TFLOP/s", "frac": round(tflops["fused"] / 157.3, 4)},
-        "best_route_TFLOPs": best,
+        "best_route_TFLOPs": best, "cpu_baseline": cpu, "sampled_parity": sampled,
         "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
-    return 0
+    return 0 if sampled is None or sampled["within_bound"] else 3
 
 
 def linear_bench(args, torch, dq4, inputs) -> int:
@@ -372,6 +463,10 @@ def linear_bench(args, torch, dq4, inputs) -> int:
     (t_call - t_fused + t_unfused) / t_call."""
     import itertools
     import math
+
+    import numpy as np
+
+    oracle_cells = []
 
     def timeit(fn, reps=20):
         for _ in range(3):
@@ -406,6 +501,8 @@ def linear_bench(args, torch, dq4, inputs) -> int:
             t_unfused = timeit(lambda: dq4.dq4_nested_dequant_unfused(
                 **dev(), offset=float(x.offset), n=n_out * n_in, blocksize=64, out_dtype=dt,
                 out=ws, scale_workspace=sw))
+            dt_name = "f16" if dt == torch.float16 else "bf16"
+            sample = None
             for op in ("forward", "grad_a"):
                 for m in (1, 16, 512, 4096):
                     k = n_in if op == "forward" else n_out
@@ -415,6 +512,8 @@ def linear_bench(args, torch, dq4, inputs) -> int:
                     t_call = timeit(lambda: dq4.dq4_dequant_linear(
                         **dev(), offset=float(x.offset), n_out=n_out, n_in=n_in, blocksize=64,
                         x=xin, op=op, y=y, w_workspace=ws))
+                    if op == "forward" and m == 16:
+                        sample = (xin, y.clone())
                     flops = 2.0 * m * n_out * n_in
                     cell = {"weight": f"{n_out}x{n_in}", "dtype": str(dt).split(".")[-1],
                             "op": op, "m": m, "call_us": round(t_call, 2),
@@ -426,17 +525,57 @@ def linear_bench(args, torch, dq4, inputs) -> int:
                                                          4)}
                     cells.append(cell)
                     print(f"[linear] {cell}", file=sys.stderr, flush=True)
-            del ws, sw
+            if not args.no_cpu:
+                # the oracle beside it, after this weight's timings: the whole
+                # weight, timed, compared bit for bit with the fused
+                # dequantization; then the forward m = 16 call against a float64
+                # product of the oracle's weight, within the FP32-accumulation
+                # and output-rounding bound
+                dq4.dq4_nested_dequant(**devs[0], offset=float(x.offset), n=n_out * n_in,
+                                       blocksize=64, out_dtype=dt, out=ws)
+                w_oracle, t_cpu = oracle_dequant_threaded(x, 0, n_out * n_in, dt_name,
+                                                          host_threads())
+                oracle_cells.append({
+                    "weight": f"{n_out}x{n_in}", "dtype": dt_name, "seconds": round(t_cpu, 4),
+                    "cores": host_threads(),
+                    "GBps": round(algorithmic_bytes(n_out * n_in, 64, 2) / t_cpu / 1e9, 3),
+                    "weight_mismatches": int(np.count_nonzero(device_bits(ws) != w_oracle))})
+                xin, y = sample
+                wt = torch.from_numpy(w_oracle.view(np.int16)).view(dt).float().numpy()
+                w64 = wt.astype(np.float64).reshape(n_out, n_in)
+                x64 = xin.float().cpu().numpy().astype(np.float64)
+                t0 = time.perf_counter()
+                ref = x64 @ w64.T
+                t_mm = time.perf_counter() - t0
+                s_abs = np.abs(x64) @ np.abs(w64).T
+                gk = n_in * 2.0 ** -24 / (1 - n_in * 2.0 ** -24)
+                u_out, tiny = ((2.0 ** -11, 2.0 ** -25) if dt == torch.float16
+                               else (2.0 ** -8, 2.0 ** -134))
+                bound = gk * s_abs + u_out * (np.abs(ref) + gk * s_abs) + tiny
+                got = y.float().cpu().numpy().astype(np.float64)
+                oracle_cells[-1]["gemm_sample"] = {
+                    "op": "forward", "m": 16, "numpy_float64_seconds": round(t_mm, 4),
+                    "max_error_over_bound": round(float((np.abs(got - ref) / bound).max()), 4)}
+                del w_oracle, wt, w64, x64, ref, s_abs, bound, got
+            del ws, sw, sample
         del devs
         torch.cuda.empty_cache()
     sp = [c["public_path_speedup"] for c in cells]
+    ok = all(c["weight_mismatches"] == 0 and c["gemm_sample"]["max_error_over_bound"] <= 1.0
+             for c in oracle_cells)
     print(json.dumps({
         "metric": "dequantize-plus-linear public-path speedup of the fused dequantization "
                   "(geomean over forward/grad_A cells)",
         "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 4), "unit": "x",
         "higher_is_better": True, "n_gpus": 1, "data": "synthetic", "cells": cells,
+        "cpu_baseline": None if args.no_cpu else {
+            "kind": "oracle", "cores": host_threads(), "cells": oracle_cells,
+            "sample": "per weight and output type: the whole weight through the C oracle "
+                      "(compared bit for bit with the fused dequantization), and the "
+                      "forward m = 16 product in numpy float64 (the call's result checked "
+                      "against it within the accumulation and output-rounding bound)"},
         "device": torch.cuda.get_device_name(0), "env": run_env(torch)}), flush=True)
-    return 0
+    return 0 if ok else 3
 
 
 def int8_prep_bench(args, torch, dq4) -> int:
@@ -445,6 +584,10 @@ def int8_prep_bench(args, torch, dq4) -> int:
     conversion, transposed copy), over the issue's benchmark grid: M in {1, 8,
     64, 512, 2048}, K = N in {3584, 4096, 8192, 14336}, L in {1, 5, 16, 64}."""
     import math
+
+    import numpy as np
+
+    import oracle
 
     r127 = 7.874015718698502e-3   # float(np.float32(1/127)): the FP32 value nearest 1/127
 
@@ -462,10 +605,13 @@ def int8_prep_bench(args, torch, dq4) -> int:
 
     g = torch.Generator(device="cuda:0").manual_seed(3)
     cells = []
+    dev_ops, dev_cb = [], {}
     for K in (3584, 4096, 8192, 14336):
         N = K
         CB = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda:0", generator=g)
         SCB = torch.rand(N, device="cuda:0", generator=g) * 10
+        if not args.no_cpu:
+            dev_cb[K] = (CB, SCB)
         for M in (1, 8, 64, 512, 2048):
             A = torch.randn((M, K), device="cuda:0", generator=g).half()
             for L in (1, 5, 16, 64):
@@ -493,18 +639,46 @@ def int8_prep_bench(args, torch, dq4) -> int:
                 torch.cuda.synchronize()
                 same = bool(torch.equal(ea.view(torch.int16), subA.view(torch.int16)) and
                             torch.equal(eb.view(torch.int16), subB.view(torch.int16)))
-                cells.append({"M": M, "K": K, "N": N, "L": L, "fused_us": round(t_f, 2),
-                              "eager_us": round(t_e, 2), "speedup": round(t_e / t_f, 3),
-                              "bit_equal_to_eager": same})
+                cell = {"M": M, "K": K, "N": N, "L": L, "fused_us": round(t_f, 2),
+                        "eager_us": round(t_e, 2), "speedup": round(t_e / t_f, 3),
+                        "bit_equal_to_eager": same}
+                cells.append(cell)
+                if not args.no_cpu:
+                    # kept on the device for the oracle pass after every GPU
+                    # timing: the timings are host-bound, so no host copies or
+                    # CPU work run between them
+                    dev_ops.append((cell, K, A, cols, subA.clone(), subB.clone()))
                 print(f"[int8] {cells[-1]}", file=sys.stderr, flush=True)
     sp = [c["speedup"] for c in cells]
+    cpu = None
+    if not args.no_cpu:
+        # the oracle beside it, on each cell's operands: one thread per call
+        def bits(t):
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        host_cb = {K: (CB.cpu().numpy(), SCB.cpu().numpy()) for K, (CB, SCB) in dev_cb.items()}
+        for cell, K, A, cols, sub_a, sub_b in dev_ops:
+            cb, scb = host_cb[K]
+            a_bits, cl, got_a, got_b = bits(A), cols.cpu().numpy(), bits(sub_a), bits(sub_b)
+            t0 = time.perf_counter()
+            oa, ob = oracle.int8_prep(a_bits, cb, scb, cl)
+            cell["oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+            cell["bit_equal_to_oracle"] = bool(np.array_equal(oa, got_a) and
+                                               np.array_equal(ob, got_b))
+        r = [c["oracle_us"] / c["fused_us"] for c in cells]
+        cpu = {"kind": "oracle", "cores": 1,
+               "oracle_us_range": [min(c["oracle_us"] for c in cells),
+                                   max(c["oracle_us"] for c in cells)],
+               "gpu_call_speedup_geomean": round(math.exp(sum(map(math.log, r)) / len(r)), 2),
+               "all_bit_equal_to_oracle": all(c["bit_equal_to_oracle"] for c in cells),
+               "sample": "every cell, one single-threaded oracle call on the same operands"}
     print(json.dumps({
         "metric": "LLM.int8 correction-operand preparation: one kernel vs the eager chain "
                   "(speedup, geomean)",
         "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 3), "unit": "x",
         "higher_is_better": True, "min_speedup": min(sp),
         "median_speedup": sorted(sp)[len(sp) // 2],
-        "all_bit_equal": all(c["bit_equal_to_eager"] for c in cells), "n_gpus": 1,
+        "all_bit_equal": all(c["bit_equal_to_eager"] for c in cells), "cpu_baseline": cpu,
+        "n_gpus": 1,
         "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0),
         "env": run_env(torch)}),
         flush=True)
@@ -523,6 +697,8 @@ def configs_bench(args, torch, dq4, inputs) -> int:
     output head's 408 MB packed weight is itself larger than the last-level
     cache, so its window loop runs on one input set, eager and per window."""
     import math
+
+    import numpy as np
 
     def graph_time(calls, inner):
         g = torch.cuda.CUDAGraph()
@@ -573,6 +749,8 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         # measure the clock ramp after each synchronization, not the kernel
         inner = n_sets * max(1, math.ceil(4000.0 / (est_us * n_sets)))
         samples = graph_time(call, inner)
+        # every set holds the same result; taken before the twin overwrites it
+        got = None if args.no_cpu else device_bits(sets[0][1])
         # the memory twin on the same sets where it applies (FP16-sized output,
         # whole 4096-element tiles): the ceiling of the access pattern at this size
         twin_us = None
@@ -585,6 +763,17 @@ def configs_bench(args, torch, dq4, inputs) -> int:
             twin_us = percentile(graph_time(twin, inner), 0.5)
         del sets
         torch.cuda.empty_cache()
+        # the oracle beside it: one threaded pass over the whole workload, and
+        # every output element compared bit for bit
+        oracle_cell = None
+        if not args.no_cpu:
+            want, t_cpu = oracle_dequant_threaded(x, 0, n, dt_name, host_threads())
+            mism = int(np.count_nonzero(got.view(np.uint32 if ob == 4 else np.uint16)
+                                        != want.view(np.uint32 if ob == 4 else np.uint16)))
+            oracle_cell = {"seconds": round(t_cpu, 4), "cores": host_threads(),
+                           "GBps": round(alg / t_cpu / 1e9, 3), "mismatches": mism}
+            del want
+        del got
         med = percentile(samples, 0.5)
         cell = {"workload": name, "n": n, "blocksize": bs, "format": x.fmt, "out": dt_name,
                 "out_shift_elements": out_shift,
@@ -594,9 +783,13 @@ def configs_bench(args, torch, dq4, inputs) -> int:
                 "frac": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "ideal_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 3),
                 "buffer_sets": n_sets, "inner": inner,
-                "memory_twin_us": None if twin_us is None else round(twin_us, 3)}
+                "memory_twin_us": None if twin_us is None else round(twin_us, 3),
+                "oracle": oracle_cell}
         print(f"[configs] {name}: {med:.2f} us, {cell['GBps']} GB/s ({cell['frac']:.3f})"
-              + ("" if twin_us is None else f", memory twin {twin_us:.2f} us"),
+              + ("" if twin_us is None else f", memory twin {twin_us:.2f} us")
+              + ("" if oracle_cell is None else
+                 f"; oracle {oracle_cell['GBps']} GB/s on {oracle_cell['cores']} threads, "
+                 f"{oracle_cell['mismatches']} mismatches"),
               file=sys.stderr, flush=True)
         return cell
 
@@ -674,8 +867,24 @@ def configs_bench(args, torch, dq4, inputs) -> int:
             "timing": "loop_us: 6 loops of the 13 launches replayed as one HIP graph, median "
                       "of >= 7 replays; eager_loop_us and per_window: eager launches with one HIP "
                       "event after each window"}
+    if not args.no_cpu:
+        # the oracle over the whole head, timed; the reused buffer still holds
+        # the last window, compared bit for bit with the oracle's rows
+        want, t_cpu = oracle_dequant_threaded(x, 0, wl.n, "f32", host_threads())
+        r0, rows = windows[-1]
+        got = device_bits(buf[: rows * wl.n_cols])
+        mism = int(np.count_nonzero(
+            got.view(np.uint32) != want[r0 * wl.n_cols:(r0 + rows) * wl.n_cols].view(np.uint32)))
+        head["oracle"] = {"seconds": round(t_cpu, 4), "cores": host_threads(),
+                          "GBps": round(alg_total / t_cpu / 1e9, 3),
+                          "compared": f"last window, rows {r0}..{r0 + rows - 1}",
+                          "mismatches": mism}
+        del want, got
     print(f"[configs] {wl.name}: {len(windows)} windows in {med_loop:.1f} us, "
-          f"{head['GBps']} GB/s ({head['frac']:.3f})", file=sys.stderr, flush=True)
+          f"{head['GBps']} GB/s ({head['frac']:.3f})"
+          + ("" if "oracle" not in head else
+             f"; oracle {head['oracle']['GBps']} GB/s, {head['oracle']['mismatches']} mismatches"),
+          file=sys.stderr, flush=True)
     del buf, dev
     print(json.dumps({
         "metric": "dequantized GB/s per workload (fraction of HBM peak)",
@@ -917,43 +1126,19 @@ def main() -> int:
     }
 
     if not args.no_cpu:
-        import concurrent.futures
-
-        import oracle
-
         got = last_out.view(torch.int16).numpy().view(np.uint16)
-
-        def oracle_pass(threads):
-            """One oracle pass over the whole tensor, split into `threads`
-            disjoint element ranges run concurrently (the C oracle releases
-            the GIL while it runs)."""
-            want = np.empty(n, dtype=np.uint16)
-            chunk = -(-n // threads)
-            chunk += (-chunk) % 8
-
-            def one(start):
-                c = min(chunk, n - start)
-                want[start:start + c] = oracle.dequant_range(
-                    x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook, x.codebook4,
-                    x.offset, start, c, bs, x.nested_blocksize, "f16")
-
-            with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as pool:
-                list(pool.map(one, range(0, n, chunk)))
-            return want
 
         def timed_passes(threads):
             passes, t_cpu, want = 0, 0.0, None
             while passes < 3 and (passes == 0 or t_cpu < args.cpu_seconds):
-                c0 = time.perf_counter()
-                want = oracle_pass(threads)
-                t_cpu += time.perf_counter() - c0
+                want, dt = oracle_dequant_threaded(x, 0, n, "f16", threads)
+                t_cpu += dt
                 passes += 1
                 print(f"[bench] oracle on {threads} thread(s), pass {passes}: {t_cpu:.2f} s so "
                       f"far", file=sys.stderr, flush=True)
             return passes, t_cpu, want
 
-        # the box's CPU share, whatever os.cpu_count() reports there
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = host_threads()
         passes, t_cpu, want = timed_passes(threads)
         passes1, t_cpu1, want1 = timed_passes(1)
         mismatches = int(np.count_nonzero(got != want))
