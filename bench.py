@@ -682,7 +682,9 @@ def int8_prep_bench(args, torch, dq4) -> int:
         "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0),
         "env": run_env(torch)}),
         flush=True)
-    return 0
+    ok = all(c["bit_equal_to_eager"] for c in cells) and (
+        cpu is None or cpu["all_bit_equal_to_oracle"])
+    return 0 if ok else 3
 
 
 def configs_bench(args, torch, dq4, inputs) -> int:
@@ -894,7 +896,9 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         "cells": cells, "output_head": head, "device": torch.cuda.get_device_name(0),
         "env": run_env(torch)}),
         flush=True)
-    return 0
+    checked = [c["oracle"] for c in cells if c["oracle"]] + (
+        [head["oracle"]] if "oracle" in head else [])
+    return 0 if all(o["mismatches"] == 0 for o in checked) else 3
 
 
 def launch_trace(args, torch, dq4, inputs) -> int:
