@@ -1,0 +1,83 @@
+"""bench.py's host logic, on the CPU: the one-GPU contract, the algorithmic
+byte counts the roofline divides by, the digest gate on counter traffic, and
+the threaded oracle used as the CPU baseline."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import oracle  # noqa: E402
+from block_wise_bit_amd import inputs  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("n,blocksize,out_bytes,want", [
+    # the per-workload algorithmic bytes of the measurement plan: packed
+    # nibbles + codes + absmax + both codebooks + output
+    (28672 * 8192, 64, 2, 590_931_008),        # headline, FP16
+    (4096 * 4096, 64, 4, 75_764_800),          # square, FP32
+    (11008 * 4096, 64, 2, 113_438_528),        # mid-size matrix, FP16/BF16
+    (11008 * 4096, 64, 4, 203_616_064),        # mid-size matrix, FP32
+    (151936 * 5376, 64, 4, 3_688_598_840),     # output head, FP32, whole
+])
+def test_algorithmic_bytes(n, blocksize, out_bytes, want):
+    assert bench.algorithmic_bytes(n, blocksize, out_bytes) == want
+
+
+def test_algorithmic_bytes_by_hand():
+    """Odd length, partial block and partial group, counted term by term."""
+    n, B = 1000, 32
+    nb = 32            # ceil(1000 / 32)
+    ng = 1             # ceil(32 / 256)
+    packed = 500       # ceil(1000 / 2)
+    want = packed + nb + 4 * ng + 4 * (256 + 16) + 2 * n
+    assert bench.algorithmic_bytes(n, B, 2) == want
+
+
+def test_traffic_is_reported_only_for_the_measured_kernel(tmp_path, monkeypatch):
+    summary = {"kernel_symbol": "k", "kernel_isa_sha256_16": "abcd" * 4,
+               "hbm_bytes_per_launch": 123456}
+    pmc = tmp_path / "pmc.json"
+    pmc.write_text(json.dumps(summary))
+    digests = tmp_path / "digests.json"
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(pmc))
+    monkeypatch.setattr(bench, "KERNEL_DIGESTS", str(digests))
+    digests.write_text(json.dumps({"k": "abcd" * 4}))
+    assert bench.measured_traffic() == 123456
+    digests.write_text(json.dumps({"k": "ffff" * 4}))     # the kernel changed since
+    assert bench.measured_traffic() is None
+    digests.write_text(json.dumps({}))                     # not built
+    assert bench.measured_traffic() is None
+    pmc.unlink()                                           # never measured
+    assert bench.measured_traffic() is None
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_threaded_oracle_equals_one_call(dt):
+    """The CPU baseline's split into disjoint element ranges on several threads
+    gives exactly the oracle's single-call output, for whole tensors and for
+    windows that start mid-byte."""
+    x = inputs.make_inputs(200_003, 64, "nf4", 0.03, seed=inputs.SEED_BASE + 90)
+    whole = oracle.dequant(x.packed, x.scale_codes, x.nested_absmax, x.scale_codebook,
+                           x.codebook4, x.offset, x.n, 64, 256, dt)
+    for first, count, threads in ((0, x.n, 7), (12345, 100_001, 3), (1, 0, 4), (5, 9, 16)):
+        got, seconds = bench.oracle_dequant_threaded(x, first, count, dt, threads)
+        assert seconds >= 0
+        assert got.dtype == whole.dtype and got.size == count
+        assert np.array_equal(got.view(np.uint8), whole[first:first + count].view(np.uint8))
