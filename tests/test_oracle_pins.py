@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import subprocess
 import shutil
 import tempfile
 
@@ -182,6 +183,55 @@ def test_conversions_exhaustive_vs_torch():
             list(pool.map(one, range(0, 1 << 32, chunk)))
     finally:
         torch.set_num_threads(os.cpu_count() or 1)
+
+
+def _f16c_library(tmpdir):
+    """tests/f16c_ref.c built for this host, or None where the CPU or compiler lacks F16C."""
+    import ctypes
+    import shutil
+    try:
+        flags = open("/proc/cpuinfo").read().split()
+    except OSError:
+        return None
+    if "f16c" not in flags or "avx" not in flags or shutil.which("gcc") is None:
+        return None
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "f16c_ref.c")
+    so = os.path.join(str(tmpdir), "libf16c_ref.so")
+    r = subprocess.run(["gcc", "-O2", "-mf16c", "-mavx", "-shared", "-fPIC", "-o", so, src],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        return None
+    lib = ctypes.CDLL(so)
+    lib.f16c_convert.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    lib.f16c_convert.restype = None
+    return lib
+
+
+def test_f16_conversion_exhaustive_vs_host_f16c(tmp_path):
+    """All 2^32 binary32 inputs: the oracle's FP16 conversion against the host
+    CPU's own converter (F16C vcvtps2ph, round to nearest even).  NaN inputs
+    must give a NaN of the same sign; their payload is not specified."""
+    f16c = _f16c_library(tmp_path)
+    if f16c is None:
+        pytest.skip("no F16C on this host")
+    lib = oracle.load()
+    chunk = 1 << 24
+
+    def one(start):
+        bits = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+        ref = np.empty(chunk, np.uint16)
+        f16c.f16c_convert(bits.ctypes.data, ref.ctypes.data, chunk)
+        got = oracle.f32_to_f16_bits(bits, oracle=lib)
+        nan_in = np.isnan(bits.view(np.float32))
+        bad = (got != ref) & ~nan_in
+        assert not bad.any(), (
+            f"{np.count_nonzero(bad)} mismatches; first input {bits[bad][0]:#010x} "
+            f"oracle {got[bad][0]:#06x} F16C {ref[bad][0]:#06x}")
+        assert _is_nan16(got[nan_in], 0x7C00).all()
+        assert ((got[nan_in] >> 15) == (bits[nan_in] >> 31)).all()
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        list(pool.map(one, range(0, 1 << 32, chunk)))
 
 
 def test_conversion_examples():
