@@ -10,6 +10,8 @@ cannot be loaded, every call raises.
     dq4_nested_dequant(packed, scale_codes, nested_absmax, scale_codebook,
                        codebook4, offset, n, blocksize, ...) -> tensor
     dq4_nested_dequant_rows(..., n_rows, n_cols, r0, rows, ...) -> tensor
+    nested_dequant(..., n, blocksize=64, dtype=None, out=None, rows=None) -> tensor
+                                                   (either of the two above, torch-style)
     dq4_rows_per_block(n_cols, elem_bytes, budget_bytes) -> int
     dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
     dq4_nested_dequant_unfused(...) -> tensor     (three-launch comparison baseline)
@@ -259,6 +261,31 @@ def dq4_nested_dequant_rows(packed, scale_codes, nested_absmax, scale_codebook, 
             _stream_handle(device, stream))
     _raise_for(st, "dq4_nested_dequant_rows")
     return out
+
+
+def nested_dequant(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                   offset: float, n: int, blocksize: int = 64, dtype=None, out=None,
+                   rows=None, stream=None):
+    """The torch-facing form of the two dequantization calls.
+
+    rows=None: the whole flat tensor of n elements (dq4_nested_dequant).
+    rows=(n_rows, n_cols, r0, count): rows [r0, r0 + count) of the
+    n_rows x n_cols weight, n == n_rows * n_cols (dq4_nested_dequant_rows).
+    dtype defaults to torch.float16.  out=None allocates the result; a given
+    out is written in place and returned.  Bad arguments and unsupported
+    layouts raise ValueError, a failed launch Dq4Error (a RuntimeError).
+    """
+    torch = _torch()
+    dtype = torch.float16 if dtype is None else dtype
+    if rows is None:
+        return dq4_nested_dequant(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                                  offset, n, blocksize, out_dtype=dtype, out=out, stream=stream)
+    n_rows, n_cols, r0, count = (int(v) for v in rows)
+    if n_rows * n_cols != int(n):
+        raise ValueError(f"rows={tuple(rows)} describes {n_rows}x{n_cols} elements, not n={n}")
+    return dq4_nested_dequant_rows(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                                   offset, n_rows, n_cols, r0, count, blocksize,
+                                   out_dtype=dtype, out=out, stream=stream)
 
 
 def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,

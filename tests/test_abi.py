@@ -221,6 +221,12 @@ def test_binding_rejects_host_tensors(lib):
     f = torch.zeros(256, dtype=torch.float32)
     with pytest.raises(ValueError):
         dq4.dq4_nested_dequant(u8, u8, f, f, f[:16], 0.0, 64, 64)
+    with pytest.raises(ValueError):
+        dq4.nested_dequant(u8, u8, f, f, f[:16], 0.0, 64)
+    with pytest.raises(ValueError):
+        dq4.nested_dequant(u8, u8, f, f, f[:16], 0.0, 64, rows=(8, 8, 0, 4))
+    with pytest.raises(ValueError):   # the window's shape does not match n
+        dq4.nested_dequant(u8, u8, f, f, f[:16], 0.0, 64, rows=(8, 9, 0, 4))
 
 
 def test_product_path_does_not_reach_the_oracle():

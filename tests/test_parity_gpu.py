@@ -276,6 +276,39 @@ def test_current_stream_ordering():
     assert_bits_equal(bits_of(res), want, "side stream")
 
 
+def test_torch_style_wrapper_matches_the_c_named_calls():
+    """nested_dequant: whole tensor and row window, allocating and in-place
+    forms, give the bits of the C-named calls and of the oracle; bad
+    arguments raise ValueError."""
+    n_rows, n_cols = 123, 1000
+    x = inputs.make_inputs(n_rows * n_cols, 128, "nf4", 0.1, seed=4242, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    whole = dq4.nested_dequant(**dev, offset=float(x.offset), n=x.n, blocksize=128)
+    assert whole.dtype == torch.float16
+    assert_bits_equal(bits_of(whole), oracle_bits(x, "f16"), "wrapper whole")
+    out = torch.empty(x.n, dtype=torch.bfloat16, device="cuda")
+    same = dq4.nested_dequant(**dev, offset=float(x.offset), n=x.n, blocksize=128,
+                              dtype=torch.bfloat16, out=out)
+    assert same.data_ptr() == out.data_ptr()
+    assert_bits_equal(bits_of(out), oracle_bits(x, "bf16"), "wrapper .out")
+    r0, count = 40, 51
+    win = dq4.nested_dequant(**dev, offset=float(x.offset), n=x.n, blocksize=128,
+                             dtype=torch.float32, rows=(n_rows, n_cols, r0, count))
+    ref = dq4.dq4_nested_dequant_rows(**dev, offset=float(x.offset), n_rows=n_rows,
+                                      n_cols=n_cols, r0=r0, rows=count, blocksize=128,
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(win.view(torch.int32), ref.view(torch.int32))
+    assert_bits_equal(bits_of(win), oracle_bits(x, "f32", r0 * n_cols, count * n_cols),
+                      "wrapper rows")
+    with pytest.raises(ValueError):
+        dq4.nested_dequant(**dev, offset=float(x.offset), n=x.n, blocksize=96)
+    with pytest.raises(ValueError):
+        dq4.nested_dequant(**dev, offset=float(x.offset), n=x.n, blocksize=128,
+                           rows=(n_rows, n_cols, 100, 24))
+
+
 def test_graph_capture_replays():
     """One call captured in a HIP graph and replayed several times, with other
     eager work in between; every replay equals the eager result."""
