@@ -222,15 +222,21 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 // nibbles from two neighbouring packed dwords, funnel-shifted by a bit
 // offset that is the same for the whole window (one dword when that offset
 // is 0), and whose elements pick one of two block scales, since a unit may
-// straddle two outer blocks.  kWhole is the instantiation for windows whose
-// units each lie in one packed dword (FP32: half of one) and one block: one
-// load and one scale per unit, as in dq4_tile_kernel.  Compiled separately,
-// it ran an 8-element output shift of the 28672 x 8192 headline shape in
-// 93.8-94.1 us against 98.9-99.1 us through the general instantiation (a
-// runtime branch inside one kernel gained nothing).  The packed bytes are
-// read through a buffer resource that ends at the last dword holding a
-// needed nibble: reads past it return zero.
-template <int OUT, bool kWhole>
+// straddle two outer blocks.  Every unit starts c = (e0 + head) mod E
+// elements past a multiple of E and outer blocks are multiples of E long, so
+// a block boundary inside a unit always falls just before its element
+// kK0 = E - c: elements below kK0 take the scale of the unit's first element,
+// the rest that of its last (the same scale when no boundary falls inside).
+// kK0 is a template parameter, so that choice costs nothing per element; a
+// per-element compare and select cost ~4 % of the launch.  kK0 == 0 is the
+// instantiation for windows whose units each lie in one packed dword (FP32:
+// half of one) and one block: one load and one scale per unit, as in
+// dq4_tile_kernel.  Compiled separately, it ran an 8-element output shift of
+// the 28672 x 8192 headline shape in 93.8-94.1 us against 98.9-99.1 us
+// through the general code (a runtime branch inside one kernel gained
+// nothing).  The packed bytes are read through a buffer resource that ends
+// at the last dword holding a needed nibble: reads past it return zero.
+template <int OUT, int kK0>
 __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_t head,
                                                                   int64_t n_full,
                                                                   int64_t n_tiles)
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_
             const int32_t byte = static_cast<int32_t>((bit >> 5) << 2);
             lo[u] = __builtin_amdgcn_raw_buffer_load_b32(src, byte, 0, kLoadPolicy);
             // with sh == 0 every unit's nibbles lie in its first dword
-            hi[u] = !kWhole && sh != 0
+            hi[u] = kK0 != 0 && sh != 0
                         ? __builtin_amdgcn_raw_buffer_load_b32(src, byte + 4, 0, kLoadPolicy)
                         : 0u;
         }
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_
             const uint32_t ul = tile_unit<OUT, kUnits>(u, t);
             const uint32_t first = r + ul * E;             // offset from block b0's start
             float v[E];
-            if constexpr (kWhole) {
+            if constexpr (kK0 == 0) {
                 // one dword (FP32: half of one) and one block per unit
                 const uint32_t word = lo[u] >> ((sh + 4 * E * ul) & 31);
                 const float s = lds_scale[first >> lb];
@@ -342,12 +348,10 @@ __global__ __launch_bounds__(kThreads) void dq4_shift_tile_kernel(Args a, int64_
                 const uint32_t ush = (sh + 4 * E * ul) & 31;  // FP32 units start mid-dword
                 const uint32_t word = __builtin_amdgcn_alignbit(hi[u], lo[u], ush);
                 const float s_lo = lds_scale[first >> lb];
-                const float s_hi = lds_scale[(first + E - 1) >> lb];
+                const float s_hi = kK0 < E ? lds_scale[(first + E - 1) >> lb] : s_lo;
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float s = ((first + e) >> lb) == (first >> lb) ? s_lo : s_hi;
-                    v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * s;
-                }
+                for (int e = 0; e < E; ++e)
+                    v[e] = lds_cb4[(word >> (4 * e)) & 0xFu] * (e < kK0 ? s_lo : s_hi);
             }
             store_unit<OUT>(dst, ul, v);
         }
@@ -475,6 +479,31 @@ bool shift_path_fits(const Args &a, int64_t out_bytes)
     return span + 8 < (int64_t{1} << 31);
 }
 
+// dq4_shift_tile_kernel<OUT, k0> for k0 in 0 .. E (E = 8 for FP16/BF16, 4
+// for FP32)
+template <int OUT>
+const void *shift_kernel(int k0)
+{
+    switch (k0) {
+    case 0: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 0>);
+    case 1: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 1>);
+    case 2: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 2>);
+    case 3: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 3>);
+    case 4: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 4>);
+    default: break;
+    }
+    if constexpr (Unit<OUT>::kElems == 8) {
+        switch (k0) {
+        case 5: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 5>);
+        case 6: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 6>);
+        case 7: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 7>);
+        case 8: return reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, 8>);
+        default: break;
+        }
+    }
+    return nullptr;
+}
+
 template <int OUT>
 dq4_status_t launch_typed(const Args &a, hipStream_t stream)
 {
@@ -501,15 +530,17 @@ dq4_status_t launch_typed(const Args &a, hipStream_t stream)
         int64_t n_tiles = n_full + (edge ? 1 : 0);  // slot 0 takes head and tail
         const int64_t grid = n_tiles < kMaxGrid ? n_tiles : kMaxGrid;
         void *params[] = {&args, &head, &n_full, &n_tiles};
-        // whole units: if the first full tile's units each lie in one packed
-        // dword and one block, every tile's do (tiles are 4096 elements apart)
+        // the first full tile decides for all (tiles are 4096 elements apart):
+        // whole units when each lies in one packed dword and one block, else
+        // the split point kK0 of every unit's elements between two blocks
         constexpr int E = Unit<OUT>::kElems;
         const int64_t e_first = a.e0 + head;
         const int64_t sh =
             (static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.packed) & 3) * 8 + 4 * e_first) & 31;
-        const bool whole = sh % (4 * E) == 0 && e_first % E == 0;
-        const void *kernel = whole ? reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, true>)
-                                   : reinterpret_cast<const void *>(&dq4_shift_tile_kernel<OUT, false>);
+        const int k0 = E - static_cast<int>(e_first % E);
+        const void *kernel = shift_kernel<OUT>(sh % (4 * E) == 0 && k0 == E ? 0 : k0);
+        if (!kernel)
+            return hip_failed(hipErrorInvalidDeviceFunction);  // k0 is always 0 .. E
         e = hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0,
                             stream);
     } else {

@@ -398,14 +398,16 @@ def test_memory_twin_writes_each_packed_word_four_times():
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("bs", [32, 64, 4096])
 @pytest.mark.parametrize("out_shift,packed_shift",
-                         [(1, 0), (0, 1), (3, 2), (5, 3), (8, 0), (4, 0), (8, 4)])
+                         [(1, 0), (0, 1), (3, 2), (5, 3), (8, 0), (4, 0), (8, 4), (2, 0),
+                          (6, 1), (7, 0)])
 def test_shifted_vector_path(dt, bs, out_shift, packed_shift):
     """Outputs shifted by out_shift elements and packed bytes by packed_shift
     bytes from their natural alignment, over 5 full tiles plus a head and a
     tail: the funnel-shifted units and two-scale elements give the oracle's
     bits.  (8, 0) and (8, 4) take the whole-unit instantiation for every
     output type, (4, 0) for FP32 (units on half dwords), the rest the
-    general one."""
+    general one; over the shifts, every split point k0 = 1 .. E of a unit's
+    elements between two blocks is taken for each output type."""
     n = 5 * 4096 + 1000 + 3
     x = inputs.make_inputs(n, bs, "nf4", -0.05, seed=77 + bs + out_shift)
     dev = dq4.to_device(x)
