@@ -33,10 +33,9 @@
  *   out             n elements of the output type, densely packed.
  * No pointer has to be aligned.  A 4-byte aligned `packed`, a 128-byte
  * aligned `out` and a window starting at a multiple of 8 elements take the
- * fastest path; other element-aligned outputs a general vector path (about
- * 2-10 % slower: least when the window's 4-bit codes fall on whole packed
- * dwords, as for a 16-byte aligned output); anything else a per-element
- * path.  All of them give bitwise identical results.
+ * fastest path; other element-aligned outputs a general vector path (a few
+ * percent slower: 2-4 % at 28672 x 8192); anything else a per-element path.
+ * All of them give bitwise identical results.
  * Input and output ranges must not overlap.
  *
  * Ownership and ordering: the library allocates nothing, frees nothing, keeps
