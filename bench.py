@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dequantized GB/s (fraction of HBM peak), NF4→FP16 28672×8192 bs64"
 HBM_PEAK_GBS = 8000.0
+MATRIX_PEAK_16BIT = 2500.0   # TFLOP/s, dense FP16/BF16 matrix cores (no sparsity)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "dq4_tile_kernel_f16_28672x8192_bs64_pmc.json")
 KERNEL_DIGESTS = os.path.join(ROOT, "block_wise_bit_amd", "libdq4_kernels.json")
 HEADLINE_KERNEL = "_ZN3dq412_GLOBAL__N_115dq4_tile_kernelILi1EEEvNS0_4ArgsEll"
@@ -289,6 +290,12 @@ def compare_unfused(args, torch, dq4, inputs) -> int:
                         "unfused_p10_p90": [round(percentile(samples["unfused"], q), 2)
                                             for q in (0.1, 0.9)],
                         "fused_GBps": round(alg / (f_med * 1e-6) / 1e9, 1),
+                        "fused_frac": round(alg / (f_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        # the unfused form also writes, rewrites and rereads the FP32
+                        # scale buffer: 16 more bytes per block
+                        "unfused_algorithmic_bytes": alg + 16 * (-(-n // 64)),
+                        "unfused_frac": round((alg + 16 * (-(-n // 64))) / (u_med * 1e-6) / 1e9
+                                              / HBM_PEAK_GBS, 4),
                         "eager_fused_us": round(med["fused_eager"], 2),
                         "eager_unfused_us": round(med["unfused_eager"], 2),
                         "eager_speedup": round(med["unfused_eager"] / med["fused_eager"], 4),
@@ -521,6 +528,11 @@ def linear_bench(args, torch, dq4, inputs) -> int:
                             "unfused_dequant_us": round(t_unfused, 2),
                             "gemm_us": round(max(t_call - t_fused, 0.0), 2),
                             "gemm_TFLOPs": round(flops / max(t_call - t_fused, 1e-3) / 1e6, 2),
+                            "gemm_frac_of_matrix_peak": round(
+                                flops / max(t_call - t_fused, 1e-3) / 1e6 / MATRIX_PEAK_16BIT, 4),
+                            "dequant_frac_of_hbm_peak": round(
+                                algorithmic_bytes(n_out * n_in, 64, 2) / (t_fused * 1e-6) / 1e9
+                                / HBM_PEAK_GBS, 4),
                             "public_path_speedup": round((t_call - t_fused + t_unfused) / t_call,
                                                          4)}
                     cells.append(cell)
@@ -605,7 +617,7 @@ def int8_prep_bench(args, torch, dq4) -> int:
 
     g = torch.Generator(device="cuda:0").manual_seed(3)
     cells = []
-    dev_ops, dev_cb = [], {}
+    dev_ops, dev_cb, roof_ops = [], {}, []
     for K in (3584, 4096, 8192, 14336):
         N = K
         CB = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda:0", generator=g)
@@ -643,12 +655,27 @@ def int8_prep_bench(args, torch, dq4) -> int:
                         "eager_us": round(t_e, 2), "speedup": round(t_e / t_f, 3),
                         "bit_equal_to_eager": same}
                 cells.append(cell)
+                roof_ops.append((cell, M, K, N, L, cols))
                 if not args.no_cpu:
                     # kept on the device for the oracle pass after every GPU
                     # timing: the timings are host-bound, so no host copies or
                     # CPU work run between them
                     dev_ops.append((cell, K, A, cols, subA.clone(), subB.clone()))
                 print(f"[int8] {cells[-1]}", file=sys.stderr, flush=True)
+    # the HBM bytes a cell must move: the outputs, and the whole 128-byte lines
+    # of A's rows (2-byte elements) and CB's rows (1-byte) that its columns
+    # fall in (every K here is a multiple of 64, so rows start on lines), plus
+    # SCB and the column list; against the call's time, which at these sizes
+    # is mostly the launch
+    for cell, M, K, N, L, cols in roof_ops:
+        cl = cols.cpu().numpy()
+        lines_a = len(set((cl * 2 // 128).tolist()))
+        lines_b = len(set((cl // 128).tolist()))
+        nbytes = 2 * (M * L + L * N) + 128 * (M * lines_a + N * lines_b) + 4 * N + 8 * L
+        cell["roofline"] = {"bound": "hbm", "bytes": nbytes,
+                            "GBps": round(nbytes / (cell["fused_us"] * 1e-6) / 1e9, 1),
+                            "frac": round(nbytes / (cell["fused_us"] * 1e-6) / 1e9
+                                          / HBM_PEAK_GBS, 4)}
     sp = [c["speedup"] for c in cells]
     cpu = None
     if not args.no_cpu:
@@ -678,6 +705,7 @@ def int8_prep_bench(args, torch, dq4) -> int:
         "higher_is_better": True, "min_speedup": min(sp),
         "median_speedup": sorted(sp)[len(sp) // 2],
         "all_bit_equal": all(c["bit_equal_to_eager"] for c in cells), "cpu_baseline": cpu,
+        "roofline_best": max((c["roofline"] for c in cells), key=lambda r: r["frac"]),
         "n_gpus": 1,
         "data": "synthetic", "cells": cells, "device": torch.cuda.get_device_name(0),
         "env": run_env(torch)}),
