@@ -158,7 +158,12 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         const int64_t tile = fs < n_paired ? xcd_paired_tile(fs, log2_share) : fs;
         const int64_t d0 = tile * kTileDwords;  // first packed dword of the tile
 
-        // 1. packed data first: the longest-latency loads
+        // 1. packed data first: the longest-latency loads.  The waves issue
+        //    this tile's loads at raised priority (an issue-arbitration hint
+        //    within the CU), ahead of waves busy in their value pass: a
+        //    workgroup's life is mostly the wait for these loads, and the
+        //    launch measured ~0.4 % faster
+        __builtin_amdgcn_s_setprio(3);
         using Word = typename Unit<OUT>::Word;
         constexpr int E = Unit<OUT>::kElems;
         constexpr int kUnits = kDwordsPerLane * 8 / E;  // units per lane and tile
@@ -189,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 
         // 3. codebooks to LDS, then every block's scale to LDS
         load_tables(a, lds_scb, lds_cb4);
+        __builtin_amdgcn_s_setprio(0);
         if (has0)
             lds_scale[t] = block_scale(lds_scb[code0], absmax0, a.offset);
         if (has1)
