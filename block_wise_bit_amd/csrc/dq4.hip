@@ -162,8 +162,10 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
         //    this tile's loads at raised priority (an issue-arbitration hint
         //    within the CU), ahead of waves busy in their value pass: a
         //    workgroup's life is mostly the wait for these loads, and the
-        //    launch measured ~0.4 % faster
-        __builtin_amdgcn_s_setprio(3);
+        //    FP16 launch measured ~0.4 % faster.  FP32 output keeps the
+        //    default priority: raised, it ran ~7 % slower
+        if constexpr (kStreamPolicy<OUT>)
+            __builtin_amdgcn_s_setprio(3);
         using Word = typename Unit<OUT>::Word;
         constexpr int E = Unit<OUT>::kElems;
         constexpr int kUnits = kDwordsPerLane * 8 / E;  // units per lane and tile
@@ -194,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void dq4_tile_kernel(Args a, int64_t n_fu
 
         // 3. codebooks to LDS, then every block's scale to LDS
         load_tables(a, lds_scb, lds_cb4);
-        __builtin_amdgcn_s_setprio(0);
+        if constexpr (kStreamPolicy<OUT>)
+            __builtin_amdgcn_s_setprio(0);
         if (has0)
             lds_scale[t] = block_scale(lds_scb[code0], absmax0, a.offset);
         if (has1)
