@@ -94,6 +94,9 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
         const Word *wp = reinterpret_cast<const Word *>(packed);
         const int64_t u0 = d0 * 8 / E;
         Word w[kUnits];
+        // the fused kernel's load-phase wave priority, for FP16/BF16 as there
+        if constexpr (kStreamPolicy<OUT>)
+            __builtin_amdgcn_s_setprio(3);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u)
             w[u] = load_packed<OUT>(tile_word<OUT, kUnits>(wp + u0, u, t));
@@ -106,6 +109,8 @@ __global__ __launch_bounds__(kThreads) void dq4_value_tile_kernel(
             lds_scale[t + kThreads] = scale[b0 + t + kThreads];
         if (t < 16)
             lds_cb4[t] = cv;
+        if constexpr (kStreamPolicy<OUT>)
+            __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         const __amdgpu_buffer_rsrc_t dst = unit_buffer(out, u0, kUnits * kThreads);
 #pragma unroll
