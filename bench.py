@@ -21,7 +21,10 @@ Prints ONE JSON line (rank 0, one GPU):
                disjoint element ranges (single_core inside: on one thread)
 Timing protocol after the bitsandbytes issue's evidence plan ("B300 evidence
 plan"): >= 20 warmups, 7 timed batches of inner launches, every batch sample
-reported with median, p10 and p90.
+reported with median, p10 and p90.  Whatever --warmup asks for, at least 20
+untimed launches and 0.1 s of them run before each timed region
+(warmup_launches in the JSON line counts them): the first milliseconds of a
+burst of launches run slower while the GPU's clocks settle.
 """
 from __future__ import annotations
 
@@ -130,6 +133,64 @@ def run_env(torch) -> dict:
             "compute_units": props.multi_processor_count,
             "library_sha256_16": lib_digest, "python": platform.python_version(),
             "host_logical_cpus": os.cpu_count()}
+
+
+# Untimed launches before any timed region, whatever --warmup asks for: at
+# least this many launches and this much GPU time.  MI355X runs the first
+# milliseconds of a burst of launches slower while its clocks settle, and the
+# bitsandbytes issue's evidence plan ("B300 evidence plan") asks for >= 20
+# warmup launches.
+WARMUP_MIN_LAUNCHES = 20
+WARMUP_MIN_SECONDS = 0.1
+
+
+def warm_up(step, asked: int, torch) -> int:
+    """Run step(k) for k = 0, 1, ... until at least max(asked, 20) launches
+    and 0.1 s have gone by (synchronizing every 20 launches); returns the
+    number of launches."""
+    want = max(int(asked), WARMUP_MIN_LAUNCHES)
+    k = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(WARMUP_MIN_LAUNCHES):
+            step(k)
+            k += 1
+        torch.cuda.synchronize()
+        if k >= want and time.perf_counter() - t0 >= WARMUP_MIN_SECONDS:
+            return k
+
+
+def raw_dequant_steps(dq4, sets, offset, n, bs, out_code, stream):
+    """step(k): dq4_nested_dequant on buffer set k mod len(sets), called
+    through the C ABI with the arguments the checked wrapper already accepted
+    for that set.  Raises on a non-OK status."""
+    import ctypes
+    lib = dq4.library()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(dev["packed"].data_ptr(), dev["scale_codes"].data_ptr(),
+              dev["nested_absmax"].data_ptr(), dev["scale_codebook"].data_ptr(),
+              dev["codebook4"].data_ptr(), ctypes.c_float(offset), n, bs, 256, out_code,
+              out.data_ptr(), handle) for dev, out in sets]
+
+    def step(k):
+        st = lib.dq4_nested_dequant(*calls[k % len(calls)])
+        if st != dq4.DQ4_OK:
+            raise RuntimeError(f"dq4_nested_dequant: {dq4.dq4_status_string(st)}")
+    return step
+
+
+def raw_twin_steps(dq4, sets, n, stream):
+    """The same for the memory twin."""
+    import ctypes
+    lib = dq4.library()
+    handle = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(dev["packed"].data_ptr(), n, out.data_ptr(), handle) for dev, out in sets]
+
+    def step(k):
+        st = lib.dq4_memory_twin_f16(*calls[k % len(calls)])
+        if st != dq4.DQ4_OK:
+            raise RuntimeError(f"dq4_memory_twin_f16: {dq4.dq4_status_string(st)}")
+    return step
 
 
 def percentile(xs, q):
@@ -1054,19 +1115,22 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     offset = float(x.offset)
 
-    def step(k):
-        dev, out = sets[k % len(sets)]
+    # every buffer set goes through the checked torch wrapper once, then the
+    # steps call the C entry point with those same, already checked arguments:
+    # the wrapper's Python checks cost tens of microseconds per call, which
+    # would leave the stream idle between launches
+    for dev, out in sets:
         dq4.dq4_nested_dequant(**dev, offset=offset, n=n, blocksize=bs, out_dtype=torch.float16,
                                out=out, stream=stream)
+    step = raw_dequant_steps(dq4, sets, offset, n, bs, dq4.DQ4_F16, stream)
 
     K = args.steps
     nbatch = max(1, min(args.batches, K))
     per = [K // nbatch + (1 if i < K % nbatch else 0) for i in range(nbatch)]
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    print(f"[bench] {args.warmup} warmup steps done", file=sys.stderr, flush=True)
+    warm = warm_up(step, args.warmup, torch)
+    print(f"[bench] {warm} warmup steps done ({args.warmup} asked for)", file=sys.stderr,
+          flush=True)
 
     # timed region: K steps in `batches` batches, one event pair per batch on
     # the launch stream, wall clock around the whole region
@@ -1098,13 +1162,10 @@ def main() -> int:
     last_out = sets[(K - 1) % len(sets)][1].cpu()
     twin_bytes = (n + 1) // 2 + 2 * n
 
-    def twin(k):
-        dev, out = sets[k % len(sets)]
+    for dev, out in sets:
         dq4.dq4_memory_twin_f16(dev["packed"], n, out=out, stream=stream)
-
-    for k in range(args.warmup):
-        twin(k)
-    torch.cuda.synchronize()
+    twin = raw_twin_steps(dq4, sets, n, stream)
+    warm_up(twin, args.warmup, torch)
     tevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(nbatch)]
     k = 0
@@ -1126,6 +1187,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_launches": warm,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",

@@ -13,6 +13,7 @@ cannot be loaded, every call raises.
     nested_dequant(..., n, blocksize=64, dtype=None, out=None, rows=None) -> tensor
                                                    (either of the two above, torch-style)
     dq4_rows_per_block(n_cols, elem_bytes, budget_bytes) -> int
+    dq4_row_window(n_rows, n_cols, elem_bytes, budget_bytes, k) -> (count, r0, rows)
     dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
     dq4_nested_dequant_unfused(...) -> tensor     (three-launch comparison baseline)
     dq4_unfused_workspace_bytes(n, blocksize) -> int
@@ -72,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.dq4_memory_twin_f16.restype = i32
     lib.dq4_rows_per_block.argtypes = [i64, i64, i64]
     lib.dq4_rows_per_block.restype = i64
+    lib.dq4_row_window.argtypes = [i64, i64, i64, i64, i64, P, P]
+    lib.dq4_row_window.restype = i64
     lib.dq4_nested_dequant_unfused.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32, P, P, P]
     lib.dq4_nested_dequant_unfused.restype = i32
     lib.dq4_unfused_workspace_bytes.argtypes = [i64, i32]
@@ -130,11 +133,24 @@ def dq4_unfused_workspace_bytes(n: int, blocksize: int) -> int:
     return int(library().dq4_unfused_workspace_bytes(int(n), int(blocksize)))
 
 
+def dq4_row_window(n_rows: int, n_cols: int, elem_bytes: int, budget_bytes: int,
+                   k: int) -> Tuple[int, int, int]:
+    """(window count, r0, rows) of window k, from the C call of the same name;
+    r0 and rows are -1 when k is not a window index."""
+    r0, rows = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    count = library().dq4_row_window(int(n_rows), int(n_cols), int(elem_bytes),
+                                     int(budget_bytes), int(k), ctypes.byref(r0),
+                                     ctypes.byref(rows))
+    return int(count), int(r0.value), int(rows.value)
+
+
 def dq4_row_windows(n_rows: int, n_cols: int, elem_bytes: int = 4,
                     budget_bytes: int = ROW_BLOCK_BUDGET_BYTES) -> List[Tuple[int, int]]:
-    """Consecutive row windows (r0, rows) of at most dq4_rows_per_block rows."""
-    rpb = dq4_rows_per_block(n_cols, elem_bytes, budget_bytes)
-    return [(r0, min(rpb, n_rows - r0)) for r0 in range(0, n_rows, rpb)]
+    """The whole row-window plan [(r0, rows), ...], window by window from
+    dq4_row_window."""
+    count = dq4_row_window(n_rows, n_cols, elem_bytes, budget_bytes, -1)[0]
+    return [dq4_row_window(n_rows, n_cols, elem_bytes, budget_bytes, k)[1:]
+            for k in range(count)]
 
 
 def _raise_for(status: int, what: str) -> None:
@@ -197,15 +213,28 @@ def _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
     return device
 
 
-def _prepare_out(out, count: int, dtype, device):
+def _prepare_out(out, count: int, dtype, device, stream=None):
     torch = _torch()
     if out is None:
-        return torch.empty(count, dtype=dtype, device=device)
+        return _used_on(torch.empty(count, dtype=dtype, device=device), stream)
     if out.device != device or out.dtype != dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of the output dtype on the inputs' device")
     if out.numel() < count:
         raise ValueError(f"out holds {out.numel()} elements, needs {count}")
     return out
+
+
+def _used_on(t, stream):
+    """Tell torch's caching allocator that the kernels enqueued on `stream`
+    use t, a tensor this module allocated on the current stream: when t is
+    freed, its memory is not handed to a new allocation until that stream's
+    work queued so far has finished.  Without it a temporary freed on return
+    could be reused by work on the current stream while a kernel on another
+    stream still reads or writes it.  (Nothing to do for the current stream,
+    whose order already covers it.)"""
+    if stream is not None and t.numel() > 0:
+        t.record_stream(stream)
+    return t
 
 
 def _stream_handle(device, stream) -> ctypes.c_void_p:
@@ -228,7 +257,7 @@ def dq4_nested_dequant(packed, scale_codes, nested_absmax, scale_codebook, codeb
     code = _out_code(out_dtype)
     device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
                            int(n), int(blocksize), int(nested_blocksize))
-    out = _prepare_out(out, max(int(n), 0), out_dtype, device)
+    out = _prepare_out(out, max(int(n), 0), out_dtype, device, stream)
     with torch.cuda.device(device):
         st = library().dq4_nested_dequant(
             packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
@@ -252,7 +281,7 @@ def dq4_nested_dequant_rows(packed, scale_codes, nested_absmax, scale_codebook, 
         raise ValueError(f"row window [{r0}, {r0 + rows}) outside 0..{n_rows}")
     device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
                            (r0 + rows) * n_cols, int(blocksize), int(nested_blocksize))
-    out = _prepare_out(out, rows * n_cols, out_dtype, device)
+    out = _prepare_out(out, rows * n_cols, out_dtype, device, stream)
     with torch.cuda.device(device):
         st = library().dq4_nested_dequant_rows(
             packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
@@ -300,10 +329,11 @@ def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codeboo
     code = _out_code(out_dtype)
     device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
                            int(n), int(blocksize), int(nested_blocksize))
-    out = _prepare_out(out, max(int(n), 0), out_dtype, device)
+    out = _prepare_out(out, max(int(n), 0), out_dtype, device, stream)
     need = dq4_unfused_workspace_bytes(int(n), int(blocksize)) // 4
     if scale_workspace is None:
-        scale_workspace = torch.empty(max(need, 1), dtype=torch.float32, device=device)
+        scale_workspace = _used_on(torch.empty(max(need, 1), dtype=torch.float32,
+                                               device=device), stream)
     elif (scale_workspace.device != device or scale_workspace.dtype != torch.float32
           or not scale_workspace.is_contiguous() or scale_workspace.numel() < need):
         raise ValueError(f"scale_workspace must be a contiguous float32 tensor of >= {need} "
@@ -319,7 +349,8 @@ def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codeboo
 
 
 def _out_prod_operands(torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4,
-                       n_rows, n_cols, blocksize, nested_blocksize, src1, src1_transposed, dst):
+                       n_rows, n_cols, blocksize, nested_blocksize, src1, src1_transposed, dst,
+                       stream):
     """Checked (device, m, ld, dst) for the two out_prod entry points."""
     device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
                            n_rows * n_cols, int(blocksize), int(nested_blocksize))
@@ -333,7 +364,7 @@ def _out_prod_operands(torch, packed, scale_codes, nested_absmax, scale_codebook
         raise ValueError(f"src1 has {k_dim} rows of the summed dimension, the weight {n_rows}")
     ld = max(int(src1.stride(0)), 1)
     if dst is None:
-        dst = torch.empty((m, n_cols), dtype=torch.float32, device=device)
+        dst = _used_on(torch.empty((m, n_cols), dtype=torch.float32, device=device), stream)
     elif (dst.device != device or dst.dtype != torch.float32 or not dst.is_contiguous()
           or dst.numel() < m * n_cols):
         raise ValueError("dst must be a contiguous float32 tensor of m * n_cols values")
@@ -365,10 +396,11 @@ def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebo
     n_rows, n_cols = int(n_rows), int(n_cols)
     device, m, ld, dst = _out_prod_operands(
         torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4, n_rows, n_cols,
-        blocksize, nested_blocksize, src1, src1_transposed, dst)
+        blocksize, nested_blocksize, src1, src1_transposed, dst, stream)
     if workspace is None:
         rows = max(1, min(n_rows, int(workspace_bytes) // max(4 * n_cols, 1)))
-        workspace = torch.empty(max(rows * n_cols, 1), dtype=torch.float32, device=device)
+        workspace = _used_on(torch.empty(max(rows * n_cols, 1), dtype=torch.float32,
+                                         device=device), stream)
     workspace = _f32_workspace(torch, workspace, device)
     with torch.cuda.device(device):
         st = library().dq4_out_prod_rows(
@@ -402,10 +434,11 @@ def dq4_out_prod_fused(packed, scale_codes, nested_absmax, scale_codebook, codeb
     n_rows, n_cols = int(n_rows), int(n_cols)
     device, m, ld, dst = _out_prod_operands(
         torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4, n_rows, n_cols,
-        blocksize, nested_blocksize, src1, src1_transposed, dst)
+        blocksize, nested_blocksize, src1, src1_transposed, dst, stream)
     if workspace is None:
         nbytes = dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, device)
-        workspace = torch.empty(max(nbytes // 4, 0), dtype=torch.float32, device=device)
+        workspace = _used_on(torch.empty(max(nbytes // 4, 0), dtype=torch.float32,
+                                         device=device), stream)
     workspace = _f32_workspace(torch, workspace, device)
     with torch.cuda.device(device):
         st = library().dq4_out_prod_fused(
@@ -443,11 +476,12 @@ def dq4_dequant_linear(packed, scale_codes, nested_absmax, scale_codebook, codeb
         raise ValueError(f"x must be a contiguous (m, {k}) tensor on the inputs' device")
     m = int(x.size(0))
     if y is None:
-        y = torch.empty((m, width), dtype=x.dtype, device=device)
+        y = _used_on(torch.empty((m, width), dtype=x.dtype, device=device), stream)
     elif y.device != device or y.dtype != x.dtype or not y.is_contiguous() or y.numel() < m * width:
         raise ValueError(f"y must be a contiguous {x.dtype} tensor of {m} x {width} values")
     if w_workspace is None:
-        w_workspace = torch.empty(max(n_out * n_in, 1), dtype=x.dtype, device=device)
+        w_workspace = _used_on(torch.empty(max(n_out * n_in, 1), dtype=x.dtype, device=device),
+                               stream)
     elif (w_workspace.device != device or w_workspace.dtype != x.dtype
           or not w_workspace.is_contiguous() or w_workspace.numel() < n_out * n_in):
         raise ValueError("w_workspace must hold n_out * n_in values of x's dtype")
@@ -461,11 +495,16 @@ def dq4_dequant_linear(packed, scale_codes, nested_absmax, scale_codebook, codeb
     return y
 
 
-def dq4_int8_prep(A, CB, SCB, cols, subA=None, subB=None, stream=None):
+def dq4_int8_prep(A, CB, SCB, cols, subA=None, subB=None, stream=None, validate=False):
     """LLM.int8 correction operands in one kernel: subA = A[:, cols] (M x L,
     FP16) and subB = fp16(fl32(fl32(CB[:, cols] * SCB[:, None]) * R127)).T
-    (L x N, FP16, contiguous).  Column indices are checked here (a host
-    synchronization) and out-of-range ones raise ValueError."""
+    (L x N, FP16, contiguous).
+
+    Asynchronous and capturable into a HIP graph: the kernel itself never
+    reads through a column index outside [0, K) and sets the outputs such an
+    index feeds to FP16 NaN.  validate=True also checks the indices on the
+    host first, raising ValueError for an out-of-range one; that check reads
+    them back, a synchronization on every call, so it is off by default."""
     torch = _torch()
     device = A.device
     if device.type != "cuda":
@@ -486,12 +525,12 @@ def dq4_int8_prep(A, CB, SCB, cols, subA=None, subB=None, stream=None):
     if CB.shape[1] != K or SCB.numel() != N:
         raise ValueError(f"CB must be N x {K} and SCB must hold N values")
     L = cols.numel()
-    if L and bool(((cols < 0) | (cols >= K)).any()):
+    if validate and L and bool(((cols < 0) | (cols >= K)).any()):
         raise ValueError(f"column indices must lie in [0, {K})")
     if subA is None:
-        subA = torch.empty((M, L), dtype=torch.float16, device=device)
+        subA = _used_on(torch.empty((M, L), dtype=torch.float16, device=device), stream)
     if subB is None:
-        subB = torch.empty((L, N), dtype=torch.float16, device=device)
+        subB = _used_on(torch.empty((L, N), dtype=torch.float16, device=device), stream)
     for name, t, numel in (("subA", subA, M * L), ("subB", subB, L * N)):
         if (t.device != device or t.dtype != torch.float16 or not t.is_contiguous()
                 or t.numel() < numel):
@@ -513,7 +552,7 @@ def dq4_memory_twin_f16(packed, n: int, out=None, stream=None):
         raise ValueError("packed must be a contiguous uint8 GPU tensor")
     if packed.numel() < -(-int(n) // 2):
         raise ValueError(f"packed holds {packed.numel()} bytes, needs {-(-int(n) // 2)}")
-    out = _prepare_out(out, max(int(n), 0), torch.float16, packed.device)
+    out = _prepare_out(out, max(int(n), 0), torch.float16, packed.device, stream)
     with torch.cuda.device(packed.device):
         st = library().dq4_memory_twin_f16(packed.data_ptr(), int(n), out.data_ptr(),
                                            _stream_handle(packed.device, stream))

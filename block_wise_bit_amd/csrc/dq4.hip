@@ -674,6 +674,24 @@ int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_by
     return r < 1 ? 1 : r;
 }
 
+int64_t dq4_row_window(int64_t n_rows, int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes,
+                       int64_t k, int64_t *r0, int64_t *rows)
+{
+    if (n_rows <= 0)
+        return 0;
+    const int64_t rpb = dq4_rows_per_block(n_cols, elem_bytes, budget_bytes);
+    const int64_t count = n_rows / rpb + (n_rows % rpb != 0 ? 1 : 0);
+    if (k >= 0 && k < count) {
+        const int64_t first = k * rpb;
+        const int64_t left = n_rows - first;
+        if (r0)
+            *r0 = first;
+        if (rows)
+            *rows = left < rpb ? left : rpb;
+    }
+    return count;
+}
+
 const char *dq4_status_string(dq4_status_t status)
 {
     switch (status) {

@@ -22,8 +22,8 @@
 //
 // Column indices are checked in the kernel: an index outside [0, K) reads
 // nothing and writes an FP16 NaN (0x7E00) to the outputs it feeds, so a bad
-// index never faults (the Python binding rejects such indices before the
-// launch).
+// index never faults (the Python binding can also reject such indices on
+// the host, on request: that check reads them back, a synchronization).
 
 #include <hip/hip_runtime.h>
 

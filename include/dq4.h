@@ -126,6 +126,20 @@ dq4_status_t dq4_nested_dequant_rows(const uint8_t *packed, const uint8_t *scale
 int64_t dq4_rows_per_block(int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes);
 
 /*
+ * The host's row-block loop of the same PR (review: the weight is walked in
+ * consecutive blocks of rows_per_block rows, the last one partial): window k
+ * of an n_rows-row weight is rows [k * rpb, k * rpb + min(rpb, n_rows - k *
+ * rpb)), rpb = dq4_rows_per_block(n_cols, elem_bytes, budget_bytes).
+ * Returns the number of windows, ceil(n_rows / rpb), or 0 for n_rows <= 0.
+ * When 0 <= k < that count, writes window k's first row to *r0 and its row
+ * count to *rows (either pointer may be NULL); otherwise writes nothing.
+ * Feeding each window to dq4_nested_dequant_rows covers every row once, in
+ * order.  Host only.
+ */
+int64_t dq4_row_window(int64_t n_rows, int64_t n_cols, int64_t elem_bytes, int64_t budget_bytes,
+                       int64_t k, int64_t *r0, int64_t *rows);
+
+/*
  * Diagnostic, not part of the method: the memory twin of the FP16 whole-tensor
  * call at block size 64.  It reads the n/2 packed bytes and writes 2n bytes
  * to `out` in exactly the tiles, tile order, load policy and store policy of

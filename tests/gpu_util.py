@@ -2,7 +2,8 @@
 same host inputs and hand back raw output bits.  No arithmetic of the method
 lives here -- the oracle computes, these functions only split ranges across
 threads and move buffers (and, for the out_prod tests, sum the oracle's
-weight against src1 in float64 with numpy)."""
+weight against src1 in float64 with numpy; the FP32 summation bounds those
+sums are checked with live in sum_bounds.py)."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -13,6 +14,7 @@ import numpy as np
 
 import block_wise_bit_amd as dq4
 import oracle
+from sum_bounds import U32, check_sum_bound  # noqa: F401  (re-exported for the GPU tests)
 
 _NP_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
 
@@ -71,33 +73,62 @@ def say(*args):
     sys.stdout.flush()
 
 
-U32 = 2.0 ** -24   # unit roundoff of binary32
-
-
 def out_prod_reference(x, n_rows, n_cols, b_rows_by_m, chunk_rows=16384):
     """float64 sum_r B[r][i] W[r][j] and sum_r |B[r][i]| |W[r][j]|, with W the
     oracle's F32 dequantization of the n_rows x n_cols weight x."""
+    parts, mag = out_prod_reference_parts(
+        x, n_cols, b_rows_by_m,
+        [(r0, min(chunk_rows, n_rows - r0)) for r0 in range(0, n_rows, chunk_rows)])
+    return sum(parts, np.zeros_like(mag)), mag
+
+
+def out_prod_reference_parts(x, n_cols, b_rows_by_m, row_ranges, chunk_rows=16384):
+    """For each (r0, rows) of row_ranges, the float64 contribution
+    sum_{r in [r0, r0+rows)} B[r][i] W[r][j]; and sum_r |B[r][i]| |W[r][j]|
+    over the union of the ranges.  W is the oracle's F32 dequantization."""
     m = b_rows_by_m.shape[1]
-    exact = np.zeros((m, n_cols))
     mag = np.zeros((m, n_cols))
-    for r0 in range(0, n_rows, chunk_rows):
-        rows = min(chunk_rows, n_rows - r0)
-        w = oracle_bits(x, "f32", r0 * n_cols, rows * n_cols).view(np.float32)
-        w = w.reshape(rows, n_cols).astype(np.float64)
-        b = b_rows_by_m[r0:r0 + rows].astype(np.float64)
-        exact += b.T @ w
-        mag += np.abs(b).T @ np.abs(w)
-    return exact, mag
+    parts = []
+    for r0, rows in row_ranges:
+        part = np.zeros((m, n_cols))
+        for c0 in range(r0, r0 + rows, chunk_rows):
+            c = min(chunk_rows, r0 + rows - c0)
+            w = oracle_bits(x, "f32", c0 * n_cols, c * n_cols).view(np.float32)
+            w = w.reshape(c, n_cols).astype(np.float64)
+            b = b_rows_by_m[c0:c0 + c].astype(np.float64)
+            part += b.T @ w
+            mag += np.abs(b).T @ np.abs(w)
+        parts.append(part)
+    return parts, mag
 
 
-def check_sum_bound(got, exact, mag, K, what, factor=1.0):
-    """Every element within factor * gamma_K * mag of the exact sum, where
-    gamma_K = K u / (1 - K u): the bound of any FP32 summation of K products,
-    in any order and with or without fused multiply-adds."""
-    gamma = K * U32 / (1 - K * U32)
-    err = np.abs(got.astype(np.float64) - exact)
-    bound = factor * gamma * mag
-    worst = np.max(err / np.maximum(bound, 1e-300))
-    say(f"{what}: max |err| {err.max():.3e}, worst err/bound {worst:.3e}")
-    assert np.isfinite(got).all(), what
-    assert (err <= bound).all(), f"{what}: error above the FP32 summation bound"
+def weight_rows(x, n_cols, rows) -> np.ndarray:
+    """The oracle's F32 weight rows `rows` (any order, repeats allowed), as a
+    len(rows) x n_cols float32 array."""
+    out = np.empty((len(rows), n_cols), np.float32)
+    for k, r in enumerate(rows):
+        out[k] = oracle_bits(x, "f32", int(r) * n_cols, n_cols, threads=1).view(np.float32)
+    return out
+
+
+def check_selection_route(route, x, n_rows, n_cols, groups, transposed, what):
+    """Full-size bit check of an out_prod route with selection-matrix src1:
+    for each group `sel` of weight rows, src1 has B[sel[i]][i] = 1 and zeros
+    elsewhere, so dst row i is one exact product 1 * W[sel[i]][j] plus exact
+    zeros -- in any summation order, row block or row split -- and must equal
+    the oracle's weight row sel[i].  dst starts as NaN, so the first row
+    block's beta = 0 must overwrite it.  Values are compared (-0.0 == +0.0:
+    a zero product may carry either sign into the sum)."""
+    import torch
+    from out_prod_cases import selection_src1
+    for g, sel in enumerate(groups):
+        b = selection_src1(n_rows, sel)
+        src1 = torch.from_numpy(np.ascontiguousarray(b.T) if transposed else b).cuda()
+        dst = torch.full((len(sel), n_cols), float("nan"), dtype=torch.float32, device="cuda")
+        y = route(src1=src1, src1_transposed=transposed, dst=dst).cpu().numpy()
+        want = weight_rows(x, n_cols, sel)
+        bad = np.argwhere(~(y == want))
+        assert bad.size == 0, (f"{what} group {g}: {bad.shape[0]} mismatches, first at (i, j) = "
+                               f"{tuple(bad[0])}, weight row {sel[bad[0][0]]}: "
+                               f"{y[tuple(bad[0])]!r} vs {want[tuple(bad[0])]!r}")
+    say(f"{what}: {len(groups)} selection calls bit-exact")

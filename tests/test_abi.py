@@ -28,7 +28,8 @@ def test_exports_every_declared_function(lib):
                           "dq4_nested_dequant_unfused", "dq4_unfused_workspace_bytes",
                           "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear",
                           "dq4_int8_prep", "dq4_out_prod_fused",
-                          "dq4_out_prod_fused_workspace_bytes", "dq4_memory_twin_f16"}
+                          "dq4_out_prod_fused_workspace_bytes", "dq4_memory_twin_f16",
+                          "dq4_row_window"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -213,6 +214,39 @@ def test_rows_per_block_worked_examples(lib):
                 assert w[-1][1] == last
     assert dq4.dq4_rows_per_block(0, 4, 1 << 28) == 1
     assert dq4.dq4_rows_per_block(256, 4, 0) == 1
+
+
+def test_row_window_plan_through_the_c_abi(lib):
+    """dq4_row_window called through ctypes on the worked examples: the
+    window count, consecutive windows that tile [0, n_rows), each of
+    rows_per_block rows but the last; out-of-range k writes nothing."""
+    with open(os.path.join(GOLDEN, "rows_per_block.txt")) as fh:
+        lines = [ln.split("#", 1)[0].split() for ln in fh]
+    for fields in (f for f in lines if f):
+        n_cols, elem, budget, n_rows, rpb, windows, last = (
+            None if v == "-" else int(v) for v in fields)
+        r0, rows = ctypes.c_int64(-7), ctypes.c_int64(-7)
+        count = lib.dq4_row_window(n_rows, n_cols, elem, budget, -1, ctypes.byref(r0),
+                                   ctypes.byref(rows))
+        assert count == windows and (r0.value, rows.value) == (-7, -7)
+        assert lib.dq4_row_window(n_rows, n_cols, elem, budget, count, ctypes.byref(r0),
+                                  ctypes.byref(rows)) == count
+        assert (r0.value, rows.value) == (-7, -7)
+        step = lib.dq4_rows_per_block(n_cols, elem, budget)
+        nxt = 0
+        for k in range(count):
+            assert lib.dq4_row_window(n_rows, n_cols, elem, budget, k, ctypes.byref(r0),
+                                      ctypes.byref(rows)) == count
+            assert r0.value == nxt
+            assert rows.value == (step if k < count - 1 else n_rows - nxt)
+            nxt += rows.value
+        assert nxt == n_rows
+        if last is not None:
+            assert rows.value == last
+        assert lib.dq4_row_window(n_rows, n_cols, elem, budget, 0, None, None) == count
+    assert lib.dq4_row_window(0, 256, 4, 1 << 28, 0, None, None) == 0
+    assert lib.dq4_row_window(-5, 256, 4, 1 << 28, 0, None, None) == 0
+    assert dq4.dq4_row_windows(5, 3, 4, 24) == [(0, 2), (2, 2), (4, 1)]
 
 
 def test_binding_rejects_host_tensors(lib):

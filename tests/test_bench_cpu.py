@@ -81,3 +81,31 @@ def test_threaded_oracle_equals_one_call(dt):
         assert seconds >= 0
         assert got.dtype == whole.dtype and got.size == count
         assert np.array_equal(got.view(np.uint8), whole[first:first + count].view(np.uint8))
+
+
+def test_warmup_floor_holds_whatever_is_asked():
+    """bench.py warms up with at least 20 launches and 0.1 s of them before a
+    timed region, even when --warmup asks for fewer (the driver's 5)."""
+    import time
+
+    class FakeCuda:
+        @staticmethod
+        def synchronize():
+            pass
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    calls = []
+
+    def step(k):
+        calls.append(k)
+        time.sleep(0.0005)
+
+    t0 = time.perf_counter()
+    done = bench.warm_up(step, 5, FakeTorch)
+    assert done == len(calls) >= bench.WARMUP_MIN_LAUNCHES
+    assert calls == list(range(done))
+    assert time.perf_counter() - t0 >= bench.WARMUP_MIN_SECONDS
+    calls.clear()
+    assert bench.warm_up(step, 250, FakeTorch) >= 250

@@ -1,12 +1,13 @@
 """Pins of the LLM.int8 correction-operand oracle (CPU only).
 
 bitsandbytes issue "Fuse LLM.int8 correction operand preparation into one
-CUDA kernel", section "Exact correctness oracle": raw-bit equality for subA;
-raw-bit FP16 equality for subB reproducing FP32 CB * SCB, then a separately
-rounded FP32 multiply by the reciprocal-127 constant, then FP16 conversion;
-coverage of the complete INT8 code domain, zero / normal /
-subnormal-adjacent / large finite SCB, L in {1, 2, 5, 16, 64}, first / last /
-non-contiguous / sorted columns and repeated indices.
+CUDA kernel", section "Exact correctness oracle": the gathered activations
+are copied bit for bit, and each weight output is the FP32 product of the
+int8 code and its row scale, multiplied again (a second rounding) by the
+FP32 constant nearest 1/127 and converted once to FP16.  That section also
+lists what the checks should reach: every int8 code, row scales of several
+kinds (zero, tiny, ordinary, huge), a range of outlier counts, and column
+sets in several orders, with repeats.
 
 The oracle (oracle/int8_prep_oracle.c) is checked against
 * the exact-rational IEEE model of tests/exact_ieee.py for every int8 code

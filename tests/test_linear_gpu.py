@@ -3,9 +3,9 @@
 bitsandbytes issue "Fuse nested scale reconstruction into SM103 4-bit
 dequantization", sections "Problem" and "Correctness requirements": the
 dequantize-plus-linear fallback and MatMul4Bit.backward's grad_A consume the
-same nested dequantization, and their results are compared "using repository
-GEMM tolerances only after the dequantized tensor itself passes bitwise
-equality".  So each case first checks the dequantized weight bit for bit
+same nested dequantization, and that page allows the usual GEMM tolerances
+for their outputs only once the dequantized weight has been shown to be
+bitwise equal.  So each case first checks the dequantized weight bit for bit
 against the oracle, then the GEMM against a float64 sum with a tolerance
 derived from the arithmetic: FP16/BF16 products are exact in FP32, an FP32
 sum of K of them is within gamma_K * S of the exact sum (gamma_K = K u /

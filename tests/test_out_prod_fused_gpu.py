@@ -11,12 +11,16 @@ Two kinds of check:
   for one row r per column i, else 0) every dst element is one exact product
   1 * W[r][j] plus exact zeros, so dst row i must equal the oracle's F32 row r
   of the weight exactly -- whatever the summation order or split;
+  This runs at full size too -- the PR's 600 000 x 256 and the 151 936 x
+  5 376 output head -- with rows chosen so that every row split of the fused
+  route (and every row block of the blocked one) is selected;
 * the sums against the oracle's weight times src1 in float64, within the
-  FP32 summation bound gamma_K * sum_r |B[r][i]| |W[r][j]| (any order, any
-  fusing), over the PR's worked example, the output head, ragged tiles, and
-  every split the workspace allows; the result is also checked to be
-  deterministic and to agree with the row-blocked route within twice the
-  bound.
+  FP32 summation bound of tests/sum_bounds.py (any order, any fusing), over
+  the PR's worked example, the output head, ragged tiles, and every split the
+  workspace allows; the result is also checked to be deterministic and to
+  agree with the row-blocked route within twice the bound.
+  tests/test_sum_bounds.py shows on the CPU that on the full-size inputs a
+  dst missing any one row block or row split fails that bound.
 """
 from __future__ import annotations
 
@@ -25,7 +29,9 @@ import pytest
 
 import block_wise_bit_amd as dq4
 from block_wise_bit_amd import inputs
-from gpu_util import check_sum_bound, oracle_bits, out_prod_reference, say
+import out_prod_cases as cases
+from gpu_util import (check_selection_route, check_sum_bound, oracle_bits, out_prod_reference,
+                      say)
 
 torch = pytest.importorskip("torch")
 
@@ -87,42 +93,85 @@ def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
                               f"vs {w[sel][tuple(bad[0])]!r}"
 
 
+def _route(dev, x, n_rows, n_cols, workspace=None):
+    def call(**kw):
+        return dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
+                                      n_cols=n_cols, blocksize=64, workspace=workspace, **kw)
+    return call
+
+
 @pytest.mark.parametrize("transposed", [False, True])
 def test_three_blocks_600000_rows_at_256_columns(transposed):
     """The PR's worked example (600 000 rows, 256 columns, m = 8), both src1
     orientations, dst prefilled with NaN."""
-    n_rows, n_cols, m = 600_000, 256, 8
-    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=600_000, n_rows=n_rows,
-                           n_cols=n_cols)
+    case = cases.PR_EXAMPLE
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
+    x = cases.pr_example_weight()
     dev = dq4.to_device(x)
-    rng = np.random.Generator(np.random.PCG64(1))
-    b = rng.standard_normal((n_rows, m)).astype(np.float32)
-    dst = torch.full((m, n_cols), float("nan"), dtype=torch.float32, device="cuda")
-    y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
-                               blocksize=64, src1=_src1(b, transposed),
-                               src1_transposed=transposed, dst=dst)
+    b = cases.random_src1(case)
+    dst = torch.full((case["m"], n_cols), float("nan"), dtype=torch.float32, device="cuda")
+    y = _route(dev, x, n_rows, n_cols)(src1=_src1(b, transposed), src1_transposed=transposed,
+                                       dst=dst)
     exact, mag = out_prod_reference(x, n_rows, n_cols, b)
     check_sum_bound(y.cpu().numpy(), exact, mag, n_rows, f"600000x256 transposed={transposed}")
+
+
+@pytest.mark.parametrize("m", [8, 128])
+@pytest.mark.parametrize("transposed", [False, True])
+def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
+    """Selection-matrix src1 at the PR's size, with the preferred row split
+    and with one split: every split and every row block is selected; dst
+    equals the weight rows exactly."""
+    case = cases.PR_EXAMPLE
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
+    x = cases.pr_example_weight()
+    dev = dq4.to_device(x)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    say(f"preferred split at m={m}: {preferred // (4 * m * n_cols)} partials")
+    assert preferred // (4 * m * n_cols) <= cases.MAX_FUSED_SPLITS
+    groups = cases.selection_groups(
+        cases.target_rows(n_rows, cases.row_windows(n_rows, n_cols)), m)
+    for ws in (None, torch.empty(0, device="cuda")):
+        check_selection_route(_route(dev, x, n_rows, n_cols, ws), x, n_rows, n_cols, groups,
+                              transposed, f"fused 600000x256 m={m} transposed={transposed} "
+                                          f"workspace={'preferred' if ws is None else 'none'}")
+
+
+@pytest.mark.parametrize("m", [16, 64, 512])
+def test_selection_output_head_is_bit_exact(m):
+    """Selection-matrix src1 over the 151 936 x 5 376 output head, both
+    orientations, at each i-tile width (16, 64 and 256 rows): every row split
+    is selected; dst equals the weight rows exactly."""
+    wl = inputs.OUTPUT_HEAD
+    x = cases.output_head_weight()
+    dev = dq4.to_device(x)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(wl.n_rows, wl.n_cols, m)
+    say(f"preferred split at m={m}: {preferred // (4 * m * wl.n_cols)} partials")
+    groups = cases.selection_groups(
+        cases.target_rows(wl.n_rows, cases.row_windows(wl.n_rows, wl.n_cols)), m)
+    for transposed in (False, True):
+        check_selection_route(_route(dev, x, wl.n_rows, wl.n_cols), x, wl.n_rows, wl.n_cols,
+                              groups, transposed,
+                              f"fused output head m={m} transposed={transposed}")
 
 
 def test_output_head_both_orientations_and_against_the_blocked_route():
     """The 151936 x 5376 output head at m = 16 in both orientations; the fused
     and the row-blocked results agree within twice the summation bound."""
-    wl = inputs.OUTPUT_HEAD
-    x = wl.inputs()
+    case = cases.OUTPUT_HEAD
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
+    x = cases.output_head_weight()
     dev = dq4.to_device(x)
-    rng = np.random.Generator(np.random.PCG64(3))
-    m = 16
-    b = rng.standard_normal((wl.n_rows, m)).astype(np.float32)
-    exact, mag = out_prod_reference(x, wl.n_rows, wl.n_cols, b)
+    b = cases.random_src1(case)
+    exact, mag = out_prod_reference(x, n_rows, n_cols, b)
     for transposed in (False, True):
         src1 = _src1(b, transposed)
-        kw = dict(offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols, blocksize=64,
+        kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64,
                   src1=src1, src1_transposed=transposed)
         fused = dq4.dq4_out_prod_fused(**dev, **kw).cpu().numpy()
-        check_sum_bound(fused, exact, mag, wl.n_rows, f"output head fused transposed={transposed}")
+        check_sum_bound(fused, exact, mag, n_rows, f"output head fused transposed={transposed}")
         blocked = dq4.dq4_out_prod_rows(**dev, **kw).cpu().numpy()
-        check_sum_bound(fused, blocked.astype(np.float64), mag, wl.n_rows,
+        check_sum_bound(fused, blocked.astype(np.float64), mag, n_rows,
                         "fused vs blocked", factor=2.0)
 
 

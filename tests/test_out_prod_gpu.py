@@ -6,13 +6,16 @@ block's GEMM accumulates into dst (beta 0, then 1).  The review says the new
 multi-block cases (600 000 rows at 256 columns: three blocks, both src1
 orientations) are the only way a wrong k-offset or a missing beta = 1 shows.
 
-Reference: the oracle's F32 dequantization of the weight (bit-exact with the
-GPU's, checked by the parity tests) times src1, summed in float64 with
-numpy -- the plain definition of the sum.  Tolerance, from the arithmetic:
-any FP32 summation of K products, in any order and with or without fused
-multiply-adds, is within gamma_K * sum_r |B[r][i]| |W[r][j]| of the exact
-sum, gamma_K = K u / (1 - K u), u = 2^-24.  The float64 reference is exact
-to far below that.
+Two kinds of check at the PR's sizes (600 000 x 256, three row blocks) and
+the output head's (151 936 x 5 376, 13 row blocks), both src1 orientations:
+* selection-matrix src1 (one 1 per column, on rows chosen so that every row
+  block, its first and last row, is hit): dst must equal the oracle's weight
+  rows exactly, so a wrong k-offset, a dropped block or a missing beta = 1
+  fails outright;
+* random src1 against the oracle's F32 weight times src1 summed in float64
+  (the plain definition of the sum), within the FP32 summation bound of
+  tests/sum_bounds.py; tests/test_sum_bounds.py shows on the CPU that on these
+  very inputs a dst missing any one row block fails that bound.
 """
 from __future__ import annotations
 
@@ -21,7 +24,8 @@ import pytest
 
 import block_wise_bit_amd as dq4
 from block_wise_bit_amd import inputs
-from gpu_util import check_sum_bound, out_prod_reference
+import out_prod_cases as cases
+from gpu_util import check_selection_route, check_sum_bound, out_prod_reference
 
 torch = pytest.importorskip("torch")
 
@@ -40,24 +44,60 @@ _reference = out_prod_reference
 _check = check_sum_bound
 
 
+def _route(dev, x, n_rows, n_cols):
+    def call(**kw):
+        return dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=n_rows,
+                                     n_cols=n_cols, blocksize=64, **kw)
+    return call
+
+
 @pytest.mark.parametrize("transposed", [False, True])
 def test_three_blocks_600000_rows_at_256_columns(transposed):
     """The worked example of the PR: 600 000 rows at 256 columns dequantize in
     three 256 MiB F32 blocks; both src1 orientations; dst prefilled with NaN so
     that the first block's beta = 0 must overwrite it."""
-    n_rows, n_cols, m = 600_000, 256, 8
+    case = cases.PR_EXAMPLE
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
     assert len(dq4.dq4_row_windows(n_rows, n_cols, 4, 256 << 20)) == 3
-    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=600_000, n_rows=n_rows,
-                           n_cols=n_cols)
+    x = cases.pr_example_weight()
     dev = dq4.to_device(x)
-    rng = np.random.Generator(np.random.PCG64(1))
-    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    b = cases.random_src1(case)
     src1 = torch.from_numpy(np.ascontiguousarray(b.T) if transposed else b).cuda()
-    dst = torch.full((m, n_cols), float("nan"), dtype=torch.float32, device="cuda")
-    y = dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
-                              blocksize=64, src1=src1, src1_transposed=transposed, dst=dst)
+    dst = torch.full((case["m"], n_cols), float("nan"), dtype=torch.float32, device="cuda")
+    y = _route(dev, x, n_rows, n_cols)(src1=src1, src1_transposed=transposed, dst=dst)
     exact, mag = _reference(x, n_rows, n_cols, b)
     _check(y.cpu().numpy(), exact, mag, n_rows, f"600000x256 transposed={transposed}")
+
+
+@pytest.mark.parametrize("m", [8, 128])
+@pytest.mark.parametrize("transposed", [False, True])
+def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
+    """Selection-matrix src1 at the PR's size: every row block (and both rows
+    at each block edge) is selected; dst equals the weight rows exactly."""
+    case = cases.PR_EXAMPLE
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
+    x = cases.pr_example_weight()
+    dev = dq4.to_device(x)
+    windows = cases.row_windows(n_rows, n_cols)
+    groups = cases.selection_groups(cases.target_rows(n_rows, windows), m)
+    check_selection_route(_route(dev, x, n_rows, n_cols), x, n_rows, n_cols, groups,
+                          transposed, f"blocked 600000x256 m={m} transposed={transposed}")
+
+
+@pytest.mark.parametrize("m", [16, 512])
+def test_selection_output_head_is_bit_exact(m):
+    """Selection-matrix src1 over the 151 936 x 5 376 output head's 13 row
+    blocks, both orientations: dst equals the weight rows exactly."""
+    wl = inputs.OUTPUT_HEAD
+    x = cases.output_head_weight()
+    dev = dq4.to_device(x)
+    windows = cases.row_windows(wl.n_rows, wl.n_cols)
+    assert len(windows) == 13
+    groups = cases.selection_groups(cases.target_rows(wl.n_rows, windows), m)
+    for transposed in (False, True):
+        check_selection_route(_route(dev, x, wl.n_rows, wl.n_cols), x, wl.n_rows, wl.n_cols,
+                              groups, transposed, f"blocked output head m={m} "
+                                                  f"transposed={transposed}")
 
 
 def test_each_block_contributes_once():
@@ -85,19 +125,16 @@ def test_each_block_contributes_once():
 
 def test_output_head_shape_both_orientations():
     """The 151936 x 5376 output head in 13 F32 windows of <= 256 MiB, m = 16."""
-    wl = inputs.OUTPUT_HEAD
-    x = wl.inputs()
+    case = cases.OUTPUT_HEAD
+    n_rows, n_cols = case["n_rows"], case["n_cols"]
+    x = cases.output_head_weight()
     dev = dq4.to_device(x)
-    rng = np.random.Generator(np.random.PCG64(3))
-    m = 16
-    b = rng.standard_normal((wl.n_rows, m)).astype(np.float32)
-    exact, mag = _reference(x, wl.n_rows, wl.n_cols, b)
+    b = cases.random_src1(case)
+    exact, mag = _reference(x, n_rows, n_cols, b)
     for transposed in (False, True):
         src1 = torch.from_numpy(np.ascontiguousarray(b.T) if transposed else b).cuda()
-        y = dq4.dq4_out_prod_rows(**dev, offset=float(x.offset), n_rows=wl.n_rows,
-                                  n_cols=wl.n_cols, blocksize=64, src1=src1,
-                                  src1_transposed=transposed)
-        _check(y.cpu().numpy(), exact, mag, wl.n_rows, f"output head transposed={transposed}")
+        y = _route(dev, x, n_rows, n_cols)(src1=src1, src1_transposed=transposed)
+        _check(y.cpu().numpy(), exact, mag, n_rows, f"output head transposed={transposed}")
 
 
 def test_blocked_equals_whole_copy_within_bound_and_edge_cases():
