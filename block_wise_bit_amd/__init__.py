@@ -16,6 +16,7 @@ cannot be loaded, every call raises.
     dq4_row_window(n_rows, n_cols, elem_bytes, budget_bytes, k) -> (count, r0, rows)
     dq4_row_windows(n_rows, n_cols, elem_bytes, budget_bytes) -> [(r0, rows)]
     dq4_nested_dequant_unfused(...) -> tensor     (three-launch comparison baseline)
+    dq4_nested_dequant_unfused_noalloc(...) -> tensor  (the same, scratch inside the library)
     dq4_unfused_workspace_bytes(n, blocksize) -> int
     dq4_out_prod_rows(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
                                                    (row-blocked out_prod, FP32 GEMM)
@@ -39,7 +40,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(PKG_DIR, "libdq4.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "dq4.h")
 
-DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP, DQ4_EBLAS = 0, 1, 2, 3, 4
+DQ4_OK, DQ4_EINVAL, DQ4_EUNSUPPORTED, DQ4_EHIP, DQ4_EBLAS, DQ4_ESCRATCH = 0, 1, 2, 3, 4, 5
+DQ4_NOALLOC_MAX_BLOCKS = 1 << 23   # outer blocks the no-allocation call's static scratch holds
 DQ4_F32, DQ4_F16, DQ4_BF16 = 0, 1, 2
 DQ4_LINEAR_FORWARD, DQ4_LINEAR_GRAD_A = 0, 1
 NESTED_BLOCKSIZE = 256
@@ -77,6 +79,9 @@ def library() -> ctypes.CDLL:
     lib.dq4_row_window.restype = i64
     lib.dq4_nested_dequant_unfused.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32, P, P, P]
     lib.dq4_nested_dequant_unfused.restype = i32
+    lib.dq4_nested_dequant_unfused_noalloc.argtypes = [P, P, P, P, P, f32, i64, i32, i32, i32,
+                                                       P, P]
+    lib.dq4_nested_dequant_unfused_noalloc.restype = i32
     lib.dq4_unfused_workspace_bytes.argtypes = [i64, i32]
     lib.dq4_unfused_workspace_bytes.restype = i64
     lib.dq4_out_prod_rows.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, P, i64, i64, i32, P,
@@ -345,6 +350,30 @@ def dq4_nested_dequant_unfused(packed, scale_codes, nested_absmax, scale_codeboo
             int(blocksize), int(nested_blocksize), code, scale_workspace.data_ptr(),
             out.data_ptr(), _stream_handle(device, stream))
     _raise_for(st, "dq4_nested_dequant_unfused")
+    return out
+
+
+def dq4_nested_dequant_unfused_noalloc(packed, scale_codes, nested_absmax, scale_codebook,
+                                       codebook4, offset: float, n: int, blocksize: int,
+                                       nested_blocksize: int = NESTED_BLOCKSIZE, out_dtype=None,
+                                       out=None, stream=None):
+    """The unfused sequence with its FP32 scales in the library's static
+    scratch instead of a workspace: the C call allocates nothing.  Pass `out`
+    to allocate nothing here either (e.g. under graph capture).  At most
+    DQ4_NOALLOC_MAX_BLOCKS outer blocks; calls that overlap on one GPU race."""
+    torch = _torch()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    code = _out_code(out_dtype)
+    device = _check_inputs(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                           int(n), int(blocksize), int(nested_blocksize))
+    out = _prepare_out(out, max(int(n), 0), out_dtype, device, stream)
+    with torch.cuda.device(device):
+        st = library().dq4_nested_dequant_unfused_noalloc(
+            packed.data_ptr(), scale_codes.data_ptr(), nested_absmax.data_ptr(),
+            scale_codebook.data_ptr(), codebook4.data_ptr(), ctypes.c_float(offset), int(n),
+            int(blocksize), int(nested_blocksize), code, out.data_ptr(),
+            _stream_handle(device, stream))
+    _raise_for(st, "dq4_nested_dequant_unfused_noalloc")
     return out
 
 

@@ -73,15 +73,24 @@ def device_assembly(workdir: str) -> str:
 
 
 def kernel_bodies(asm: str) -> dict:
-    """{kernel symbol: its instructions, comments and directives dropped}."""
+    """{kernel symbol: its instructions up to its first s_endpgm, comments,
+    directives and labels dropped}.  Only symbols the assembly declares as
+    functions count (a device variable's label is data, not a kernel)."""
+    functions = set(re.findall(r"^\s*\.type\s+(_Z\w+),@function", asm, flags=re.M))
     bodies = {}
-    for m in re.finditer(r"^(_Z\w+):.*?$(.*?)^\s*s_endpgm", asm, flags=re.M | re.S):
-        lines = []
-        for line in m.group(2).splitlines():
-            code = line.split(";")[0].strip()
-            if code and not code.startswith(".") and not code.endswith(":"):
-                lines.append(code)
-        bodies[m.group(1)] = "\n".join(lines)
+    current, lines = None, []
+    for line in asm.splitlines():
+        if current is None:
+            m = re.match(r"^(_Z\w+):", line)
+            if m and m.group(1) in functions:
+                current, lines = m.group(1), []
+            continue
+        code = line.split(";")[0].strip()
+        if code.startswith("s_endpgm"):
+            bodies[current] = "\n".join(lines)
+            current = None
+        elif code and not code.startswith(".") and not code.endswith(":"):
+            lines.append(code)
     return bodies
 
 

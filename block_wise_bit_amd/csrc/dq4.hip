@@ -705,6 +705,8 @@ const char *dq4_status_string(dq4_status_t status)
         return "DQ4_EHIP: kernel launch failed";
     case DQ4_EBLAS:
         return "DQ4_EBLAS: library GEMM failed";
+    case DQ4_ESCRATCH:
+        return "DQ4_ESCRATCH: more outer blocks than the static scratch holds";
     default:
         return "DQ4: unknown status";
     }

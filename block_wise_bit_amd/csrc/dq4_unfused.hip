@@ -25,6 +25,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "dq4.h"
 #include "dq4_device.h"
 
@@ -174,6 +177,114 @@ hipError_t launch_value(const uint8_t *packed, const float *scale, const float *
                            dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, stream);
 }
 
+// The three launches over a caller-provided FP32 scale buffer of
+// ceil(n / 2^log2_block) values (arguments already validated).
+dq4_status_t launch_unfused(const uint8_t *packed, const uint8_t *scale_codes,
+                            const float *nested_absmax, const float *scale_codebook,
+                            const float *codebook4, float offset, int64_t n, int log2_block,
+                            int32_t out_dtype, float *scale_workspace, void *out,
+                            hipStream_t s)
+{
+    int64_t n_blocks = ((n - 1) >> log2_block) + 1;
+    const int64_t grid = (n_blocks + kThreads - 1) / kThreads;
+    if (grid > 0x7FFFFFFF)
+        return DQ4_EINVAL;
+    {
+        void *params[] = {&scale_codes, &nested_absmax, &scale_codebook, &scale_workspace,
+                          &n_blocks};
+        const hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void *>(&dq4_scale_codes_kernel),
+                            dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, s);
+        if (e != hipSuccess)
+            return hip_failed(e);
+    }
+    {
+        void *params[] = {&scale_workspace, &offset, &n_blocks};
+        const hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void *>(&dq4_add_offset_kernel),
+                            dim3(static_cast<uint32_t>(grid)), dim3(kThreads), params, 0, s);
+        if (e != hipSuccess)
+            return hip_failed(e);
+    }
+    hipError_t e;
+    switch (out_dtype) {
+    case DQ4_F32:
+        e = launch_value<DQ4_F32>(packed, scale_workspace, codebook4, out, n, log2_block, s);
+        break;
+    case DQ4_F16:
+        e = launch_value<DQ4_F16>(packed, scale_workspace, codebook4, out, n, log2_block, s);
+        break;
+    default:
+        e = launch_value<DQ4_BF16>(packed, scale_workspace, codebook4, out, n, log2_block, s);
+        break;
+    }
+    if (e != hipSuccess)
+        return hip_failed(e);
+    return DQ4_OK;
+}
+
+// Validation shared by both unfused entry points (the workspace pointer
+// aside); sets *log2_block.
+dq4_status_t validate_unfused(const uint8_t *packed, const uint8_t *scale_codes,
+                              const float *nested_absmax, const float *scale_codebook,
+                              const float *codebook4, int64_t n, int32_t blocksize,
+                              int32_t nested_blocksize, int32_t out_dtype, const void *out,
+                              int *log2_block)
+{
+    const dq4_status_t st = validate_layout(blocksize, nested_blocksize, out_dtype, log2_block);
+    if (st != DQ4_OK)
+        return st;
+    if (n < 0 || n > kMaxElems)
+        return DQ4_EINVAL;
+    if (n == 0)
+        return DQ4_OK;
+    if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 || !out)
+        return DQ4_EINVAL;
+    return DQ4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of dq4_nested_dequant_unfused_noalloc: the FP32 block scales of up
+// to DQ4_NOALLOC_MAX_BLOCKS outer blocks (32 MiB), a file-scope device array
+// that each GPU the library runs on holds until the process ends.  In host
+// code `scratch` only names the symbol; its device address, one per device,
+// comes from hipGetSymbolAddress on that device's first call and is the only
+// form in which it reaches a kernel or any other HIP call.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) float scratch[DQ4_NOALLOC_MAX_BLOCKS];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<float *> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// This device's address of `scratch` (looked up once per device).
+dq4_status_t scratch_on_current_device(float **ptr)
+{
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return hip_failed(e);
+    if (device < 0 || device >= kMaxScratchDevices)
+        return DQ4_EUNSUPPORTED;
+    float *p = g_scratch[device].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[device].load(std::memory_order_relaxed);
+        if (!p) {
+            void *addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return hip_failed(e);
+            if (!addr)
+                return hip_failed(hipErrorInvalidSymbol);
+            p = static_cast<float *>(addr);
+            g_scratch[device].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return DQ4_OK;
+}
+
 }  // namespace
 }  // namespace dq4
 
@@ -195,54 +306,40 @@ dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *sc
 {
     int log2_block = 0;
     const dq4_status_t st =
-        dq4::validate_layout(blocksize, nested_blocksize, out_dtype, &log2_block);
-    if (st != DQ4_OK)
+        dq4::validate_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4, n,
+                              blocksize, nested_blocksize, out_dtype, out, &log2_block);
+    if (st != DQ4_OK || n == 0)
         return st;
-    if (n < 0 || n > dq4::kMaxElems)
+    if (!scale_workspace)
         return DQ4_EINVAL;
-    if (n == 0)
-        return DQ4_OK;
-    if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 ||
-        !scale_workspace || !out)
-        return DQ4_EINVAL;
+    return dq4::launch_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                               offset, n, log2_block, out_dtype, scale_workspace, out,
+                               static_cast<hipStream_t>(stream));
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int64_t n_blocks = (n + blocksize - 1) / blocksize;
-    const int64_t grid = (n_blocks + dq4::kThreads - 1) / dq4::kThreads;
-    if (grid > 0x7FFFFFFF)
-        return DQ4_EINVAL;
-    {
-        void *params[] = {&scale_codes, &nested_absmax, &scale_codebook, &scale_workspace,
-                          &n_blocks};
-        const hipError_t e =
-            hipLaunchKernel(reinterpret_cast<const void *>(&dq4::dq4_scale_codes_kernel),
-                            dim3(static_cast<uint32_t>(grid)), dim3(dq4::kThreads), params, 0, s);
-        if (e != hipSuccess)
-            return dq4::hip_failed(e);
-    }
-    {
-        void *params[] = {&scale_workspace, &offset, &n_blocks};
-        const hipError_t e =
-            hipLaunchKernel(reinterpret_cast<const void *>(&dq4::dq4_add_offset_kernel),
-                            dim3(static_cast<uint32_t>(grid)), dim3(dq4::kThreads), params, 0, s);
-        if (e != hipSuccess)
-            return dq4::hip_failed(e);
-    }
-    hipError_t e;
-    switch (out_dtype) {
-    case DQ4_F32:
-        e = dq4::launch_value<DQ4_F32>(packed, scale_workspace, codebook4, out, n, log2_block, s);
-        break;
-    case DQ4_F16:
-        e = dq4::launch_value<DQ4_F16>(packed, scale_workspace, codebook4, out, n, log2_block, s);
-        break;
-    default:
-        e = dq4::launch_value<DQ4_BF16>(packed, scale_workspace, codebook4, out, n, log2_block, s);
-        break;
-    }
-    if (e != hipSuccess)
-        return dq4::hip_failed(e);
-    return DQ4_OK;
+dq4_status_t dq4_nested_dequant_unfused_noalloc(const uint8_t *packed,
+                                                const uint8_t *scale_codes,
+                                                const float *nested_absmax,
+                                                const float *scale_codebook,
+                                                const float *codebook4, float offset, int64_t n,
+                                                int32_t blocksize, int32_t nested_blocksize,
+                                                int32_t out_dtype, void *out, void *stream)
+{
+    int log2_block = 0;
+    const dq4_status_t st =
+        dq4::validate_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4, n,
+                              blocksize, nested_blocksize, out_dtype, out, &log2_block);
+    if (st != DQ4_OK || n == 0)
+        return st;
+    if (((n - 1) >> log2_block) + 1 > DQ4_NOALLOC_MAX_BLOCKS)
+        return DQ4_ESCRATCH;
+    float *scales = nullptr;
+    const dq4_status_t sst = dq4::scratch_on_current_device(&scales);
+    if (sst != DQ4_OK)
+        return sst;
+    return dq4::launch_unfused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
+                               offset, n, log2_block, out_dtype, scales, out,
+                               static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -68,8 +68,14 @@ enum {
     DQ4_EUNSUPPORTED = 2,  /* blocksize not a power of two in [32, 4096], or
                               nested_blocksize other than 256 */
     DQ4_EHIP = 3,          /* the kernel launch failed */
-    DQ4_EBLAS = 4          /* the library GEMM (rocBLAS) failed */
+    DQ4_EBLAS = 4,         /* the library GEMM (rocBLAS) failed */
+    DQ4_ESCRATCH = 5       /* the call needs more than the library's static
+                              scratch holds (dq4_nested_dequant_unfused_noalloc) */
 };
+
+/* Outer blocks whose FP32 scales fit in the static scratch of
+ * dq4_nested_dequant_unfused_noalloc (32 MiB per device). */
+#define DQ4_NOALLOC_MAX_BLOCKS (1 << 23)
 
 enum {
     DQ4_F32 = 0,
@@ -175,6 +181,34 @@ dq4_status_t dq4_nested_dequant_unfused(const uint8_t *packed, const uint8_t *sc
                                         float offset, int64_t n, int32_t blocksize,
                                         int32_t nested_blocksize, int32_t out_dtype,
                                         float *scale_workspace, void *out, void *stream);
+
+/*
+ * dq4_nested_dequant_unfused without a workspace argument, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (less
+ * scale_workspace), same three kernels, same results, bit for bit.
+ *
+ * The FP32 scale buffer is a static device array inside the library,
+ * DQ4_NOALLOC_MAX_BLOCKS floats (32 MiB), one copy per GPU, held from the
+ * first call on that GPU until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine); its first call on a
+ * device looks up that device's address of the array (hipGetSymbolAddress).
+ *
+ * Limit: ceil(n / blocksize) <= DQ4_NOALLOC_MAX_BLOCKS, else DQ4_ESCRATCH
+ * and nothing is enqueued (e.g. n <= 2^29 at blocksize 64).  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams or threads) race and give wrong results; serialize
+ * them.  Nothing in the array needs to start at zero: the first kernel
+ * writes every scale the third one reads.  Other errors as for
+ * dq4_nested_dequant_unfused.
+ */
+dq4_status_t dq4_nested_dequant_unfused_noalloc(const uint8_t *packed,
+                                                const uint8_t *scale_codes,
+                                                const float *nested_absmax,
+                                                const float *scale_codebook,
+                                                const float *codebook4, float offset, int64_t n,
+                                                int32_t blocksize, int32_t nested_blocksize,
+                                                int32_t out_dtype, void *out, void *stream);
 
 /* Bytes of FP32 scale workspace dq4_nested_dequant_unfused needs: 4 * ceil(n /
  * blocksize); 0 for non-positive arguments or n above 2^62.  Host only. */

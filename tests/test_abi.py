@@ -29,7 +29,7 @@ def test_exports_every_declared_function(lib):
                           "dq4_out_prod_rows", "dq4_last_blas_status", "dq4_dequant_linear",
                           "dq4_int8_prep", "dq4_out_prod_fused",
                           "dq4_out_prod_fused_workspace_bytes", "dq4_memory_twin_f16",
-                          "dq4_row_window"}
+                          "dq4_row_window", "dq4_nested_dequant_unfused_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
     # and the binding keeps the C names
@@ -38,7 +38,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for st in (dq4.DQ4_OK, dq4.DQ4_EINVAL, dq4.DQ4_EUNSUPPORTED, dq4.DQ4_EHIP, dq4.DQ4_EBLAS, 99):
+    for st in (dq4.DQ4_OK, dq4.DQ4_EINVAL, dq4.DQ4_EUNSUPPORTED, dq4.DQ4_EHIP, dq4.DQ4_EBLAS,
+               dq4.DQ4_ESCRATCH, 99):
         s = dq4.dq4_status_string(st)
         assert s.startswith("DQ4")
     assert dq4.dq4_last_hip_error() == 0
@@ -87,6 +88,30 @@ def test_validation_unfused(lib):
     assert dq4.dq4_unfused_workspace_bytes(1025, 64) == 4 * 17
     assert dq4.dq4_unfused_workspace_bytes(0, 64) == 0
     assert dq4.dq4_unfused_workspace_bytes((1 << 63) - 1, 64) == 0   # no overflow
+
+
+def test_validation_unfused_noalloc(lib):
+    """The allocation-free call rejects more outer blocks than its static
+    scratch holds, before touching the GPU; other checks as for the unfused
+    call."""
+    p = ctypes.c_void_p(1)
+
+    def call(n=64, blocksize=64, nested=256, dtype=dq4.DQ4_F16, out=p, ptr=p):
+        return lib.dq4_nested_dequant_unfused_noalloc(ptr, p, p, p, p, ctypes.c_float(0.0), n,
+                                                      blocksize, nested, dtype, out, None)
+    limit = dq4.DQ4_NOALLOC_MAX_BLOCKS
+    assert limit == 1 << 23
+    assert call(n=0) == dq4.DQ4_OK
+    assert call(n=-5) == dq4.DQ4_EINVAL
+    assert call(out=None) == dq4.DQ4_EINVAL
+    assert call(ptr=None) == dq4.DQ4_EINVAL
+    assert call(blocksize=100) == dq4.DQ4_EUNSUPPORTED
+    assert call(nested=64) == dq4.DQ4_EUNSUPPORTED
+    assert call(dtype=9) == dq4.DQ4_EINVAL
+    assert call(n=limit * 32 + 1, blocksize=32) == dq4.DQ4_ESCRATCH      # one block too many
+    assert call(n=limit * 4096 + 1, blocksize=4096) == dq4.DQ4_ESCRATCH
+    assert call(n=(1 << 62), blocksize=64) == dq4.DQ4_ESCRATCH
+    assert "scratch" in dq4.dq4_status_string(dq4.DQ4_ESCRATCH)
 
 
 def test_validation_out_prod(lib):

@@ -1,0 +1,84 @@
+"""The allocation-free unfused call, dq4_nested_dequant_unfused_noalloc (GPU).
+
+Called through the C ABI (ctypes, no torch wrapper) and compared bit for bit
+with the existing dq4_nested_dequant_unfused -- which takes a caller-owned
+workspace -- on the same inputs, over consecutive calls that shrink: the
+first uses the whole static scratch (DQ4_NOALLOC_MAX_BLOCKS outer blocks),
+each later one is smaller, so stale scales from a larger call stay in the
+scratch beyond what the smaller call writes.  The smallest case is also
+checked against the oracle.  One call past the limit is rejected with
+DQ4_ESCRATCH and writes nothing.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import block_wise_bit_amd as dq4
+from block_wise_bit_amd import inputs
+from gpu_util import assert_bits_equal, bits_of, oracle_bits, say, torch_dtype
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+CODES = {"f32": dq4.DQ4_F32, "f16": dq4.DQ4_F16, "bf16": dq4.DQ4_BF16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from libs import ensure_hip_library
+    ensure_hip_library()
+
+
+def _noalloc(dev, x, dt, out):
+    lib = dq4.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return lib.dq4_nested_dequant_unfused_noalloc(
+        dev["packed"].data_ptr(), dev["scale_codes"].data_ptr(), dev["nested_absmax"].data_ptr(),
+        dev["scale_codebook"].data_ptr(), dev["codebook4"].data_ptr(), ctypes.c_float(x.offset),
+        x.n, x.blocksize, x.nested_blocksize, CODES[dt], out.data_ptr(), stream)
+
+
+# (n, blocksize, format, offset, output type): shrinking calls; the first
+# fills the scratch exactly, the last is odd-length (per-element path)
+CALLS = [
+    (dq4.DQ4_NOALLOC_MAX_BLOCKS * 32, 32, "nf4", 0.03, "f16"),
+    (28672 * 8192, 64, "nf4", 0.03, "bf16"),
+    ((1 << 22) + 37, 128, "fp4", -0.02, "f32"),
+    (4099, 32, "nf4", 0.1, "f16"),
+]
+
+
+def test_matches_the_workspace_call_on_shrinking_calls():
+    for k, (n, bs, fmt, off, dt) in enumerate(CALLS):
+        say(f"no-alloc call {k}: n={n} bs={bs} {fmt} {dt}")
+        x = inputs.make_inputs(n, bs, fmt, off, seed=inputs.SEED_BASE + 700 + k)
+        dev = dq4.to_device(x)
+        assert x.n_blocks <= dq4.DQ4_NOALLOC_MAX_BLOCKS
+        want = dq4.dq4_nested_dequant_unfused(**dev, offset=float(x.offset), n=n, blocksize=bs,
+                                              out_dtype=torch_dtype(dt))
+        out = torch.full((n,), float("nan"), dtype=torch_dtype(dt), device="cuda")
+        assert _noalloc(dev, x, dt, out) == dq4.DQ4_OK
+        torch.cuda.synchronize()
+        assert_bits_equal(bits_of(out), bits_of(want), f"no-alloc call {k} vs workspace call")
+        if n < 1 << 23:
+            assert_bits_equal(bits_of(out), oracle_bits(x, dt), f"no-alloc call {k} vs oracle")
+        del dev, want, out
+        torch.cuda.empty_cache()
+
+
+def test_past_the_limit_is_rejected_and_writes_nothing():
+    n, bs = dq4.DQ4_NOALLOC_MAX_BLOCKS * 32 + 1, 32
+    x = inputs.make_inputs(n, bs, "nf4", 0.03, seed=inputs.SEED_BASE + 799)
+    dev = dq4.to_device(x)
+    out = torch.full((n,), 7.0, dtype=torch.float16, device="cuda")
+    assert _noalloc(dev, x, "f16", out) == dq4.DQ4_ESCRATCH
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    with pytest.raises(ValueError, match="scratch"):
+        dq4.dq4_nested_dequant_unfused_noalloc(**dev, offset=0.03, n=n, blocksize=bs, out=out)
