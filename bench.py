@@ -679,6 +679,8 @@ def int8_prep_bench(args, torch, dq4) -> int:
     g = torch.Generator(device="cuda:0").manual_seed(3)
     cells = []
     dev_ops, dev_cb, roof_ops = [], {}, []
+    # --int8-k / --int8-l restrict the grid (the random draws stay those of the
+    # whole grid, so a restricted cell has the same operands as in a full run)
     for K in (3584, 4096, 8192, 14336):
         N = K
         CB = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda:0", generator=g)
@@ -689,6 +691,8 @@ def int8_prep_bench(args, torch, dq4) -> int:
             A = torch.randn((M, K), device="cuda:0", generator=g).half()
             for L in (1, 5, 16, 64):
                 cols = torch.randperm(K, device="cuda:0", generator=g)[:L].sort().values
+                if (args.int8_k and K != args.int8_k) or (args.int8_l and L != args.int8_l):
+                    continue
                 subA = torch.empty((M, L), dtype=torch.float16, device="cuda:0")
                 subB = torch.empty((L, N), dtype=torch.float16, device="cuda:0")
                 lib = dq4.library()
@@ -706,7 +710,7 @@ def int8_prep_bench(args, torch, dq4) -> int:
                     return ea, eb
 
                 t_f = timeit(fused)
-                t_e = timeit(eager)
+                t_e = timeit(eager) if not args.int8_fused_only else float("nan")
                 ea, eb = eager()
                 fused()
                 torch.cuda.synchronize()
@@ -1055,6 +1059,12 @@ def main() -> int:
     ap.add_argument("--int8-prep", action="store_true",
                     help="instead of the benchmark, time the LLM.int8 correction-operand "
                          "preparation against the eager chain")
+    ap.add_argument("--int8-k", type=int, default=0,
+                    help="--int8-prep: only the cells with this K (= N)")
+    ap.add_argument("--int8-l", type=int, default=0,
+                    help="--int8-prep: only the cells with this many outlier columns")
+    ap.add_argument("--int8-fused-only", action="store_true",
+                    help="--int8-prep: time the one-kernel call only (for counter runs)")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the benchmark, time every dequantization workload (square, "
                          "mid matrix, headline, block-size sweep, output-head window loop) "
