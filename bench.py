@@ -427,9 +427,12 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
               src1=src1)
 
     def timeit(fn, reps):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
+        # each route is warmed on its own before it is timed: at least 20
+        # calls and 0.1 s of them (the GPU's clocks after the previous
+        # route's different load take a while to settle; measured: the fused
+        # route at m = 64 took 1.10 ms over 7 calls right after the blocked
+        # route, 0.94 ms once warmed)
+        warm_up(lambda k: fn(), 0, torch)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
@@ -450,7 +453,7 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
                                         n_cols=wl.n_cols, r0=r0, rows=rows, blocksize=64,
                                         out_dtype=torch.float32, out=ws)
 
-    reps = max(3, args.steps // 100)
+    reps = max(20, args.steps // 35)
     t_blocked = timeit(blocked, reps)
     out_blocked = dst.clone()
     t_fused = timeit(fused, reps)
@@ -537,9 +540,7 @@ def linear_bench(args, torch, dq4, inputs) -> int:
     oracle_cells = []
 
     def timeit(fn, reps=20):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(lambda k: fn(), 0, torch)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
@@ -800,9 +801,7 @@ def configs_bench(args, torch, dq4, inputs) -> int:
         with torch.cuda.graph(g):
             for k in range(inner):
                 calls(k)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
+        warm_up(lambda k: g.replay(), 0, torch)
         samples = []
         for _ in range(max(7, args.batches)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
