@@ -106,6 +106,13 @@ struct Shape {
     static constexpr int kLdsB = kTileI + 4;                 // padded LDS row of src1 values
     static constexpr int kB = kStage * kTileI / kThreads;    // src1 values per lane and stage
     using Acc = typename std::conditional<kSmall, f32x4, f32x16>::type;
+    // Accumulator sets per block.  The 16-row tile has only two blocks per
+    // wave, so with one set each MFMA of a stage waited on the one just
+    // issued before it, and the compiler shuffled the accumulators between
+    // registers on every stage; consecutive steps in alternate sets (added
+    // together at the end) remove both (~3 % at m <= 16).  The wider tiles
+    // already interleave enough blocks.
+    static constexpr int kSets = kSmall ? 2 : 1;
 
     // one MFMA: acc += A (kBlk x kK) x B (kK x kBlk); lane l holds A[l % kBlk][l / kBlk]
     // and B[l / kBlk][l % kBlk]
@@ -273,7 +280,8 @@ template <int kTileI>
 __device__ __forceinline__ void mma_stage(
     const float (*lds_w)[kLdsW], const float (*lds_b)[Shape<kTileI>::kLdsB], int wi, int wj,
     int kl, int cl,
-    typename Shape<kTileI>::Acc (&acc)[Shape<kTileI>::kBlocksI][Shape<kTileI>::kBlocksJ])
+    typename Shape<kTileI>::Acc (&acc)[Shape<kTileI>::kSets][Shape<kTileI>::kBlocksI]
+                                      [Shape<kTileI>::kBlocksJ])
 {
     using S = Shape<kTileI>;
     const int ia = S::kWaveI * wi + cl, jw = S::kWaveJ * wj + cl;
@@ -295,11 +303,12 @@ __device__ __forceinline__ void mma_stage(
             for (int bj = 0; bj < S::kBlocksJ; ++bj)
                 wv[nxt][bj] = lds_w[kk + S::kK + kl][jw + S::kBlk * bj];
         }
+        const int set = (kk / S::kK) % S::kSets;
 #pragma unroll
         for (int bi = 0; bi < S::kBlocksI; ++bi)
 #pragma unroll
             for (int bj = 0; bj < S::kBlocksJ; ++bj)
-                acc[bi][bj] = S::mma(av[cur][bi], wv[cur][bj], acc[bi][bj]);
+                acc[set][bi][bj] = S::mma(av[cur][bi], wv[cur][bj], acc[set][bi][bj]);
         if (kk + S::kK < kStage) {
             // keep the next step's LDS reads ahead of this step's MFMAs (the
             // compiler otherwise issues them just before their use)
@@ -336,12 +345,14 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
 
     const int wi = wave % S::kWavesI, wj = wave / S::kWavesI;
     const int kl = lane / S::kBlk, cl = lane % S::kBlk;
-    typename S::Acc acc[S::kBlocksI][S::kBlocksJ];
+    typename S::Acc acc[S::kSets][S::kBlocksI][S::kBlocksJ];
 #pragma unroll
-    for (int bi = 0; bi < S::kBlocksI; ++bi)
+    for (int q = 0; q < S::kSets; ++q)
 #pragma unroll
-        for (int bj = 0; bj < S::kBlocksJ; ++bj)
-            acc[bi][bj] = typename S::Acc{};
+        for (int bi = 0; bi < S::kBlocksI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < S::kBlocksJ; ++bj)
+                acc[q][bi][bj] = typename S::Acc{};
 
     StageLoad<kTileI> ld;
     load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, i0, j0, t, ld);
@@ -381,7 +392,13 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
             for (int bj = 0; bj < S::kBlocksJ; ++bj) {
                 const int64_t j = j0 + S::kWaveJ * wj + S::kBlk * bj + cl;
                 if (j < a.n_cols)
-                    out[i * a.n_cols + j] = acc[bi][bj][v];
+                {
+                    float sum = acc[0][bi][bj][v];
+#pragma unroll
+                    for (int q = 1; q < S::kSets; ++q)
+                        sum = sum + acc[q][bi][bj][v];
+                    out[i * a.n_cols + j] = sum;
+                }
             }
         }
 }
