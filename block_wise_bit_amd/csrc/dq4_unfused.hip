@@ -251,7 +251,7 @@ dq4_status_t validate_unfused(const uint8_t *packed, const uint8_t *scale_codes,
 // comes from hipGetSymbolAddress on that device's first call and is the only
 // form in which it reaches a kernel or any other HIP call.
 // ---------------------------------------------------------------------------
-__device__ __align__(256) float scratch[DQ4_NOALLOC_MAX_BLOCKS];
+static __device__ __align__(256) float scratch[DQ4_NOALLOC_MAX_BLOCKS];
 
 constexpr int kMaxScratchDevices = 64;
 std::atomic<float *> g_scratch[kMaxScratchDevices];

@@ -39,7 +39,10 @@
  * Input and output ranges must not overlap.
  *
  * Ownership and ordering: the library allocates nothing, frees nothing, keeps
- * no handle to any buffer and never synchronizes.  Each fused call enqueues
+ * no handle to any buffer and never synchronizes.  (Two exceptions, each
+ * documented at its call: the GEMM routes keep a rocBLAS handle per thread and
+ * device, and dq4_nested_dequant_unfused_noalloc uses a static device array
+ * that the runtime sets up with the library's code.)  Each fused call enqueues
  * exactly one kernel on `stream` (a hipStream_t; NULL means the legacy
  * default stream) and returns; the output is ready when that stream reaches
  * the kernel.  Calls are reentrant and thread-safe.
