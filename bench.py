@@ -1077,7 +1077,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); the "
+        print(f"bench.py: measures one GPU only (asked for {args.gpus}); the "
               "dequantization shards without any exchange, so there is no multi-GPU step to time.",
               file=sys.stderr)
         return 2
