@@ -82,3 +82,48 @@ def test_past_the_limit_is_rejected_and_writes_nothing():
     assert bool((out == 7.0).all())
     with pytest.raises(ValueError, match="scratch"):
         dq4.dq4_nested_dequant_unfused_noalloc(**dev, offset=0.03, n=n, blocksize=bs, out=out)
+
+
+def test_captured_in_a_graph_replays_bit_exact():
+    """The call the entry point exists for: captured into a HIP graph on
+    torch's capture stream (through the C ABI, into preallocated buffers),
+    then replayed three times with new inputs copied in eagerly between
+    replays; each replay equals the workspace call on the same inputs, bit
+    for bit."""
+    n, bs, dt = (1 << 22) + 4096, 64, "bf16"
+    first = inputs.make_inputs(n, bs, "nf4", 0.03, seed=inputs.SEED_BASE + 800)
+    dev = dq4.to_device(first)
+    out = torch.empty((n,), dtype=torch_dtype(dt), device="cuda")
+    lib = dq4.library()
+
+    def call():
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return lib.dq4_nested_dequant_unfused_noalloc(
+            dev["packed"].data_ptr(), dev["scale_codes"].data_ptr(),
+            dev["nested_absmax"].data_ptr(), dev["scale_codebook"].data_ptr(),
+            dev["codebook4"].data_ptr(), ctypes.c_float(first.offset), n, bs,
+            first.nested_blocksize, CODES[dt], out.data_ptr(), stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the device's first call: the scratch address lookup
+        assert call() == dq4.DQ4_OK
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert call() == dq4.DQ4_OK
+    for rep in range(3):
+        x = inputs.make_inputs(n, bs, "fp4" if rep % 2 else "nf4", 0.03,
+                               seed=inputs.SEED_BASE + 801 + rep)
+        for name, t in dq4.to_device(x).items():
+            dev[name].copy_(t)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = dq4.dq4_nested_dequant_unfused(**dev, offset=float(first.offset), n=n,
+                                              blocksize=bs, out_dtype=torch_dtype(dt))
+        torch.cuda.synchronize()
+        assert_bits_equal(bits_of(out), bits_of(want), f"graph replay {rep}")
+        say(f"no-alloc graph replay {rep}: bit-exact")
