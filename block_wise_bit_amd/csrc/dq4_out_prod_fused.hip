@@ -35,7 +35,15 @@
 //  * two LDS buffers: the waves decode the next stage into one while the
 //    MFMAs read the other, and the global loads of the stage after that are
 //    issued before the barrier, so each stage costs one barrier and its
-//    loads fly during the next stage's MFMAs;
+//    loads fly during the next stage's MFMAs; the stage loop is unrolled by
+//    two, so every LDS address is a lane-constant register plus an
+//    immediate;
+//  * every stage but a split's last holds kStage rows of the split: on the
+//    aligned path its loads are a uniform base plus a lane-constant 32-bit
+//    offset, with no bounds checks (lanes past n_cols or m read in-range
+//    bytes whose products land only in dst elements that are never stored),
+//    which halves the vector instructions of a stage (9 % faster at m = 64,
+//    2-11 % at the other widths); the last stage keeps the checked loads;
 //  * the rows are split when that fills the GPU's resident workgroup slots
 //    (sized from the kernel's occupancy) better than the tiles alone; each
 //    split writes its partial tile to the caller's workspace, and a second
@@ -62,7 +70,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileJ = 128;         // dst columns (weight columns) per workgroup
-constexpr int kStage = 16;          // weight rows per LDS stage
+constexpr int kLog2Stage = 4;
+constexpr int kStage = 1 << kLog2Stage;  // weight rows per LDS stage
 constexpr int kLdsW = kTileJ + 4;   // padded LDS row of decoded weights
 constexpr int64_t kMinRowsPerSplit = 256;
 constexpr int64_t kMaxSplits = 64;
@@ -88,6 +97,7 @@ struct FusedArgs {
     int log2_block;
     int tiles_i;
     int tiles_j;
+    int full_stages;         // 1: full stages take the unchecked loads (offsets fit 32 bits)
 };
 
 // Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
@@ -123,6 +133,11 @@ struct Shape {
     // out: its 2 KiB of LDS would cost that tile a resident workgroup per CU
     // (2 % slower at m = 512).
     static constexpr bool kPairTable = kTileI != 256;
+    // Waves per SIMD the register allocation must allow: the wide tiles'
+    // LDS already caps them at 2 (256 rows) and 4 (128 rows) per SIMD, and
+    // left alone the compiler spends registers on hoisted LDS addresses until
+    // fewer fit.  The narrow tiles are left to the compiler.
+    static constexpr int kMinWaves = kTileI == 256 ? 2 : kTileI == 128 ? 4 : 1;
 
     // one MFMA: acc += A (kBlk x kK) x B (kK x kBlk); lane l holds A[l % kBlk][l / kBlk]
     // and B[l / kBlk][l % kBlk]
@@ -152,6 +167,10 @@ struct StageLoad {
     float absmax_lo, absmax_hi;
     float b[Shape<kTileI>::kB];
 };
+
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ void load_stage_b(const FusedArgs &a, int64_t k0, int64_t k_end,
+                                             int64_t i0, int t, StageLoad<kTileI> &ld);
 
 // kAligned8: n_cols % 8 == 0 and packed 4-byte aligned, so a lane's 8
 // consecutive elements are one aligned packed dword and are all in range
@@ -186,6 +205,15 @@ __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64
             ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
         }
     }
+    load_stage_b<kTileI, kSrc1Transposed>(a, k0, k_end, i0, t, ld);
+}
+
+// The src1 values of one stage, with bounds checks: B[r][i] for the stage's
+// rows below k_end and columns below m, 0 elsewhere.
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ void load_stage_b(const FusedArgs &a, int64_t k0, int64_t k_end,
+                                             int64_t i0, int t, StageLoad<kTileI> &ld)
+{
     constexpr int kB = Shape<kTileI>::kB;
     if constexpr (!kSrc1Transposed) {
         // B[r][i] = src1[r * ld + i]: one stage row, kB consecutive columns
@@ -220,6 +248,53 @@ __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64
     }
 }
 
+// The 8 weights of one packed dword (element 2p in the low nibble of byte
+// p, element 2p + 1 in its high nibble), all in the block of scale s:
+// v[q] = fl32(codebook4[nibble q] * s).  With the pair table, one 8-byte LDS
+// read returns both entries of a byte.
+template <int kTileI>
+__device__ __forceinline__ void decode8(uint32_t packed4, float s, const float *lds_cb4,
+                                        const f32x2 *lds_pair, float (&v)[8])
+{
+    if constexpr (Shape<kTileI>::kPairTable) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t off = ((packed4 >> (8 * p)) & 0xFFu) << 3;
+            const f32x2 e = *reinterpret_cast<const f32x2 *>(
+                reinterpret_cast<const char *>(lds_pair) + off);
+            v[2 * p] = e.x * s;
+            v[2 * p + 1] = e.y * s;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t k = (packed4 >> (4 * q)) & 0xFu;
+            v[q] = lds_cb4[k] * s;
+        }
+    }
+}
+
+// The lane's src1 values of one stage into LDS (lds_b[r][i] = B[r][i]).
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ void store_stage_b(int t, const StageLoad<kTileI> &ld,
+                                              float (*lds_b)[Shape<kTileI>::kLdsB])
+{
+    constexpr int kB = Shape<kTileI>::kB;
+    if constexpr (!kSrc1Transposed) {
+        constexpr int kLanesPerRow = kTileI / kB;
+        const int br = t / kLanesPerRow, bc = (t % kLanesPerRow) * kB;
+#pragma unroll
+        for (int q = 0; q < kB; ++q)
+            lds_b[br][bc + q] = ld.b[q];
+    } else {
+        constexpr int kLanesPerCol = kStage / kB;
+        const int bc = t / kLanesPerCol, br = (t % kLanesPerCol) * kB;
+#pragma unroll
+        for (int q = 0; q < kB; ++q)
+            lds_b[br + q][bc] = ld.b[q];
+    }
+}
+
 template <int kTileI, bool kSrc1Transposed, bool kAligned8>
 __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
                                              int64_t j0, int t, const StageLoad<kTileI> &ld,
@@ -234,24 +309,8 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     float v[8];
     if (r < k_end && j < a.n_cols) {
         const float s_lo = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
-        if constexpr (kAligned8 && Shape<kTileI>::kPairTable) {
-            // one block for all 8 elements (see load_stage); byte p holds
-            // elements 2p (low nibble) and 2p + 1
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t off = ((ld.packed4 >> (8 * p)) & 0xFFu) << 3;
-                const f32x2 e = *reinterpret_cast<const f32x2 *>(
-                    reinterpret_cast<const char *>(lds_pair) + off);
-                v[2 * p] = e.x * s_lo;
-                v[2 * p + 1] = e.y * s_lo;
-            }
-        } else if constexpr (kAligned8) {
-            // one block for all 8 elements (see load_stage)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t k = (ld.packed4 >> (4 * q)) & 0xFu;
-                v[q] = lds_cb4[k] * s_lo;
-            }
+        if constexpr (kAligned8) {
+            decode8<kTileI>(ld.packed4, s_lo, lds_cb4, lds_pair, v);  // one block (see load_stage)
         } else {
             const int lb = a.log2_block;
             const int64_t e = r * a.n_cols + j;
@@ -277,20 +336,137 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         lds_w[row][col + q] = v[q];
+    store_stage_b<kTileI, kSrc1Transposed>(t, ld, lds_b);
+}
+
+// Full stages of the aligned path.  A stage is full when all kStage of its
+// rows are in the split; every stage but a split's last is.  Each address of
+// a full stage is a uniform base (scalar registers, advanced per stage) plus
+// a lane-constant 32-bit offset, so the loads spend no vector instructions
+// on 64-bit index arithmetic and the stage needs no bounds checks: lanes
+// whose weight columns lie past n_cols load column j0's bytes instead, and
+// lanes whose src1 column lies past m (transposed src1) load column i0's;
+// those values only reach dst columns and rows that are never stored (the
+// MFMA's output column j depends on weight column j alone, its row i on src1
+// column i alone).  The host takes this path only when the offsets fit.
+struct LaneMap {
+    uint32_t w_elem;   // the lane's first weight element, from the stage's first
+    uint32_t w_byte;   // its packed byte, w_elem / 2 (w_elem is a multiple of 8)
+    uint32_t b_byte;   // the lane's first src1 value, bytes from the stage's first
+    bool b_whole;      // the tile's src1 values are all in range (uniform; else
+                       // the checked loads of src1, for a ragged last tile of m)
+};
+
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ LaneMap lane_map(const FusedArgs &a, int64_t i0, int64_t j0, int t)
+{
+    LaneMap ln;
+    const int col = (t & 15) * 8;
+    const uint32_t col_in = j0 + col < a.n_cols ? static_cast<uint32_t>(col) : 0u;
+    ln.w_elem = static_cast<uint32_t>(t >> 4) * static_cast<uint32_t>(a.n_cols) + col_in;
+    ln.w_byte = ln.w_elem >> 1;
     constexpr int kB = Shape<kTileI>::kB;
+    const uint32_t ld = static_cast<uint32_t>(a.ld);
     if constexpr (!kSrc1Transposed) {
         constexpr int kLanesPerRow = kTileI / kB;
-        const int br = t / kLanesPerRow, bc = (t % kLanesPerRow) * kB;
-#pragma unroll
-        for (int q = 0; q < kB; ++q)
-            lds_b[br][bc + q] = ld.b[q];
+        const uint32_t ib = static_cast<uint32_t>((t % kLanesPerRow) * kB);
+        ln.b_byte = 4u * (static_cast<uint32_t>(t / kLanesPerRow) * ld + ib);
+        ln.b_whole = i0 + kTileI <= a.m;
     } else {
         constexpr int kLanesPerCol = kStage / kB;
-        const int bc = t / kLanesPerCol, br = (t % kLanesPerCol) * kB;
-#pragma unroll
-        for (int q = 0; q < kB; ++q)
-            lds_b[br + q][bc] = ld.b[q];
+        const uint32_t ic = static_cast<uint32_t>(t / kLanesPerCol);
+        const uint32_t ic_in = i0 + ic < a.m ? ic : 0u;
+        ln.b_byte = 4u * (ic_in * ld + static_cast<uint32_t>((t % kLanesPerCol) * kB));
+        ln.b_whole = true;
     }
+    return ln;
+}
+
+// A raw buffer over `bytes` bytes from `base`.  A full stage's loads go
+// through buffers whose base is the stage's uniform address, so each load
+// is one scalar base plus the lane's 32-bit offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_buffer(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(bytes), kRawBufferWord3);
+}
+
+// The float at byte_offset + extra; `extra` is a compile-time constant that
+// goes into the instruction's scalar offset, not into a vector register.
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t buf, uint32_t byte_offset,
+                                          int extra = 0)
+{
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(buf, byte_offset, extra, 0));
+}
+
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ void load_full_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
+                                                int64_t i0, int64_t j0, int t,
+                                                const LaneMap &ln, StageLoad<kTileI> &ld)
+{
+    const int lb = a.log2_block;
+    const uint32_t n_cols = static_cast<uint32_t>(a.n_cols);
+    const int64_t e0 = k0 * a.n_cols + j0;  // a multiple of 8
+    ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(
+        span_buffer(a.packed + (e0 >> 1), kStage / 2 * n_cols), ln.w_byte, 0, 0);
+    // block of the lane's 8 elements, (e0 + w_elem) >> lb: a uniform part bh
+    // and the lane's part c
+    const int64_t bh = e0 >> lb;
+    const uint32_t bl = static_cast<uint32_t>(e0 & ((int64_t{1} << lb) - 1));
+    const uint32_t c = (bl + ln.w_elem) >> lb;
+    const uint32_t c_span = ((kStage * n_cols + 4095u) >> lb) + 1u;
+    ld.code_lo = __builtin_amdgcn_raw_buffer_load_b8(span_buffer(a.scale_codes + bh, c_span), c,
+                                                     0, 0);
+    const uint32_t g =
+        (static_cast<uint32_t>(bh & ((1 << kNestedLog2) - 1)) + c) >> kNestedLog2;
+    const uint32_t g_span = 4u * ((c_span + 255u) / 256u + 1u);
+    ld.absmax_lo = load_f32(span_buffer(a.nested_absmax + (bh >> kNestedLog2), g_span), 4u * g);
+    constexpr int kB = Shape<kTileI>::kB;
+    if (ln.b_whole) {
+        const uint32_t ld_src1 = static_cast<uint32_t>(a.ld);
+        const __amdgpu_buffer_rsrc_t b =
+            kSrc1Transposed
+                ? span_buffer(a.src1 + (i0 * a.ld + k0), 4u * (kTileI * ld_src1 + kStage))
+                : span_buffer(a.src1 + (k0 * a.ld + i0), 4u * (kStage * ld_src1 + kTileI));
+        if constexpr (kB % 4 == 0) {
+            // kB consecutive floats: 16-byte loads (dword alignment suffices).
+            // The whole vector is cast at once: casting its lanes one by one
+            // let this compiler shrink the load to its first dword.
+#pragma unroll
+            for (int q = 0; q < kB; q += 4) {
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(b, ln.b_byte, 4 * q, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ld.b[q + e] = v[e];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kB; ++q)
+                ld.b[q] = load_f32(b, ln.b_byte, 4 * q);
+        }
+    } else {
+        load_stage_b<kTileI, kSrc1Transposed>(a, k0, k_end, i0, t, ld);
+    }
+}
+
+template <int kTileI, bool kSrc1Transposed>
+__device__ __forceinline__ void decode_full_stage(const FusedArgs &a, int t,
+                                                  const StageLoad<kTileI> &ld,
+                                                  const float *lds_scb, const float *lds_cb4,
+                                                  const f32x2 *lds_pair,
+                                                  float (*lds_w)[kLdsW],
+                                                  float (*lds_b)[Shape<kTileI>::kLdsB])
+{
+    const int row = t >> 4, col = (t & 15) * 8;
+    const float s = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
+    float v[8];
+    decode8<kTileI>(ld.packed4, s, lds_cb4, lds_pair, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        lds_w[row][col + q] = v[q];
+    store_stage_b<kTileI, kSrc1Transposed>(t, ld, lds_b);
 }
 
 // The MFMAs of one stage: acc[bi][bj] += A(i block bi) x W(j block bj) over
@@ -341,9 +517,12 @@ __device__ __forceinline__ void mma_stage(
 }
 
 // Two LDS buffers: while the waves multiply one stage, they decode the next
-// into the other buffer, so one barrier per stage suffices.
+// into the other buffer, so one barrier per stage suffices.  The stage loop
+// is unrolled by two, so that each step's LDS buffers are known at compile
+// time and every LDS address is a lane-constant register plus an immediate.
 template <int kTileI, bool kSrc1Transposed, bool kAligned8>
-__global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<kTileI>::kMinWaves)))
+void out_prod_fused_kernel(FusedArgs a)
 {
     using S = Shape<kTileI>;
     __shared__ float lds_w[2][kStage][kLdsW];
@@ -379,31 +558,75 @@ __global__ __launch_bounds__(kThreads) void out_prod_fused_kernel(FusedArgs a)
             for (int bj = 0; bj < S::kBlocksJ; ++bj)
                 acc[q][bi][bj] = typename S::Acc{};
 
+    // stage s holds rows k_begin + kStage * s ..; the first n_full stages are
+    // full and, on the aligned path when the host allows it, take the
+    // unchecked loads
+    // (stage counts are below 2^31: the host caps the rows of a split)
+    const int64_t rows = k_end - k_begin;  // > 0
+    const int n_stages =
+        __builtin_amdgcn_readfirstlane(static_cast<int>((rows + kStage - 1) >> kLog2Stage));
+    const int n_full = kAligned8 && a.full_stages
+                           ? __builtin_amdgcn_readfirstlane(static_cast<int>(rows >> kLog2Stage))
+                           : 0;
+    LaneMap ln{};
+    if constexpr (kAligned8)
+        ln = lane_map<kTileI, kSrc1Transposed>(a, i0, j0, t);
+
     StageLoad<kTileI> ld;
-    load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, i0, j0, t, ld);
-    __syncthreads();  // the codebooks are in LDS
-    decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin, k_end, j0, t, ld, lds_scb, lds_cb4, lds_pair,
-                                          lds_w[0], lds_b[0]);
-    if (k_begin + kStage < k_end)
-        load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin + kStage, k_end, i0, j0, t, ld);
-    __syncthreads();
-    // at the top of each pass: the stage at k0 is in buffer p, `ld` holds the
-    // stage at k0 + kStage (if any)
-    int p = 0;
-    for (int64_t k0 = k_begin; k0 < k_end; k0 += kStage, p ^= 1) {
+    const auto load = [&](int s) {
+        const int64_t k0 = k_begin + kStage * s;
+        if constexpr (kAligned8) {
+            if (s < n_full) {
+                load_full_stage<kTileI, kSrc1Transposed>(a, k0, k_end, i0, j0, t, ln, ld);
+                return;
+            }
+        }
+        load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0, k_end, i0, j0, t, ld);
+    };
+    const auto decode = [&](int s, auto buffer) {
+        constexpr int q = decltype(buffer)::value;
+        if constexpr (kAligned8) {
+            if (s < n_full) {
+                decode_full_stage<kTileI, kSrc1Transposed>(a, t, ld, lds_scb, lds_cb4, lds_pair,
+                                                           lds_w[q], lds_b[q]);
+                return;
+            }
+        }
+        decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin + kStage * s, k_end, j0, t,
+                                                         ld, lds_scb, lds_cb4, lds_pair,
+                                                         lds_w[q], lds_b[q]);
+    };
+    // one step: the MFMAs of stage s (in buffer q), then stage s + 1 decoded
+    // into the other buffer and the loads of stage s + 2 issued
+    const auto step = [&](int s, auto buffer) {
+        constexpr int q = decltype(buffer)::value;
         // a wave issuing MFMAs goes first among the SIMD's waves, so the matrix
         // unit is fed while other waves decode (~2 % at m >= 512)
         __builtin_amdgcn_s_setprio(1);
-        mma_stage<kTileI>(lds_w[p], lds_b[p], wi, wj, kl, cl, acc);
+        mma_stage<kTileI>(lds_w[q], lds_b[q], wi, wj, kl, cl, acc);
         __builtin_amdgcn_s_setprio(0);
-        if (k0 + kStage < k_end) {
-            decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0 + kStage, k_end, j0, t, ld, lds_scb,
-                                                  lds_cb4, lds_pair, lds_w[p ^ 1], lds_b[p ^ 1]);
-            if (k0 + 2 * kStage < k_end)
-                load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0 + 2 * kStage, k_end, i0, j0, t, ld);
+        if (s + 1 < n_stages) {
+            decode(s + 1, std::integral_constant<int, q ^ 1>{});
+            if (s + 2 < n_stages)
+                load(s + 2);
         }
         __syncthreads();
+    };
+
+    load(0);
+    __syncthreads();  // the codebooks are in LDS
+    decode(0, std::integral_constant<int, 0>{});
+    if (n_stages > 1)
+        load(1);
+    __syncthreads();
+    // even stages in buffer 0, odd ones in buffer 1
+    int s = 0;
+    for (; s + 1 < n_stages; s += 2) {
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
     }
+    if (s < n_stages)
+        step(s, std::integral_constant<int, 0>{});
 
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
 #pragma unroll
@@ -554,6 +777,21 @@ int64_t rows_per_split(int64_t n_rows, int64_t tiles, int64_t resident, int64_t 
     return ceil_div(ceil_div(n_rows, splits), kStage) * kStage;
 }
 
+// Whether full stages may take the unchecked loads: the lane-constant offsets
+// of LaneMap and the block arithmetic of load_full_stage stay below 2^32
+// (weights: kStage rows of n_cols elements plus a block offset under 4096;
+// src1: kStage rows, or tile_i columns when transposed, of ld floats).
+bool full_stages_fit(int64_t n_cols, int64_t ld, int tile_i, bool transposed)
+{
+    constexpr int64_t k32 = int64_t{1} << 32;
+    if (n_cols >= k32 / kStage || kStage * n_cols + 4096 >= k32)
+        return false;
+    const int64_t rows = transposed ? tile_i : kStage;
+    if (ld >= k32 / 4 / rows)
+        return false;
+    return 4 * (rows * ld + tile_i + kStage) < k32;
+}
+
 dq4_status_t grid_size(int64_t count, int device, uint32_t *grid)
 {
     int64_t g = ceil_div(count, kThreads);
@@ -644,12 +882,15 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     const int64_t rps = dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
     const int64_t splits = dq4::ceil_div(n_rows, rps);
     const int64_t groups = splits * tiles_i * tiles_j;
-    if (groups > 0x7FFFFFFF)
-        return DQ4_EUNSUPPORTED;
+    if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kStage) > 0x7FFFFFFF)
+        return DQ4_EUNSUPPORTED;  // the kernel counts a split's stages in 32 bits
 
+    const bool full = aligned8 && dq4::full_stages_fit(n_cols, ld_src1, plan.tile_i,
+                                                       src1_transposed != 0);
     dq4::FusedArgs a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, src1,
                      splits > 1 ? workspace : dst, n_rows, n_cols, m, ld_src1, rps, offset,
-                     log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j)};
+                     log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j),
+                     full ? 1 : 0};
     void *params[] = {&a};
     e = hipLaunchKernel(plan.kernel, dim3(static_cast<uint32_t>(groups)), dim3(dq4::kThreads),
                         params, 0, s);

@@ -93,6 +93,62 @@ def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
                               f"vs {w[sel][tuple(bad[0])]!r}"
 
 
+@pytest.mark.parametrize("transposed", [False, True])
+@pytest.mark.parametrize("m", [5, 16, 70, 150])
+def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
+    """The kernel's full stages load without bounds checks: lanes past n_cols
+    or past m read in-range elements whose products only reach dst elements
+    that are never stored.  Here src1's padding (ld > m, or ld > n_rows when
+    transposed) holds NaN, the weight's last 128-column tile is ragged and its
+    last 16-row stage partial; a NaN that reached a stored element's sum
+    would show, so dst row i must equal the oracle's weight row sel[i]."""
+    n_rows, n_cols = 16 * 37 + 5, 400
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=777, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(m))
+    sel = rng.choice(n_rows, m, replace=m > n_rows)
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    shape = (m, n_rows) if transposed else (n_rows, m)
+    padded = torch.full((shape[0], shape[1] + 9), float("nan"), device="cuda")
+    src1 = padded[:, :shape[1]]
+    src1.copy_(_src1(b, transposed))
+    for ws in (None, torch.empty(0, device="cuda")):
+        y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                                   blocksize=64, src1=src1, src1_transposed=transposed,
+                                   workspace=ws).cpu().numpy()
+        bad = np.argwhere(y != w[sel])
+        assert bad.size == 0, f"first mismatch at (i, j) = {bad[0]}: {y[tuple(bad[0])]!r}"
+
+
+def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
+    """A transposed src1 whose leading dimension puts its 16 columns of a
+    tile more than 2^32 bytes apart: the unchecked stages' 32-bit lane
+    offsets would not fit, so every stage takes the checked loads; the bits
+    equal those of the same call on a compact src1 and the oracle's rows."""
+    n_rows, n_cols, m = 16 * 9 + 3, 256, 2
+    ld = (1 << 26) + 64
+    x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", -0.03, seed=778, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    sel = np.array([n_rows - 1, 7])
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    flat = torch.full(((m - 1) * ld + n_rows,), float("nan"), device="cuda")
+    wide = flat.as_strided((m, n_rows), (ld, 1))
+    wide.copy_(_src1(b, True))
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64,
+              src1_transposed=True)
+    y_wide = dq4.dq4_out_prod_fused(**dev, **kw, src1=wide).cpu().numpy()
+    y_compact = dq4.dq4_out_prod_fused(**dev, **kw, src1=_src1(b, True)).cpu().numpy()
+    assert np.array_equal(y_wide.view(np.uint32), y_compact.view(np.uint32))
+    assert np.array_equal(y_wide, w[sel])
+    del flat, wide
+
+
 def _route(dev, x, n_rows, n_cols, workspace=None):
     def call(**kw):
         return dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
