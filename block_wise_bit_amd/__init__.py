@@ -391,7 +391,9 @@ def _out_prod_operands(torch, packed, scale_codes, nested_absmax, scale_codebook
     k_dim = int(src1.size(1) if src1_transposed else src1.size(0))
     if k_dim != n_rows:
         raise ValueError(f"src1 has {k_dim} rows of the summed dimension, the weight {n_rows}")
-    ld = max(int(src1.stride(0)), 1)
+    # a single row's stride is arbitrary (numpy and torch leave it so): its
+    # leading dimension is then the row length
+    ld = max(int(src1.stride(0)) if src1.size(0) > 1 else int(src1.size(1)), 1)
     if dst is None:
         dst = _used_on(torch.empty((m, n_cols), dtype=torch.float32, device=device), stream)
     elif (dst.device != device or dst.dtype != torch.float32 or not dst.is_contiguous()

@@ -44,6 +44,10 @@
 //    bytes whose products land only in dst elements that are never stored),
 //    which halves the vector instructions of a stage (9 % faster at m = 64,
 //    2-11 % at the other widths); the last stage keeps the checked loads;
+//  * decode-sized m (at most 16) on the aligned path takes a narrow kernel
+//    that decodes each packed dword straight into the matrix instruction's
+//    operand registers, with no LDS staging of the weights and no barrier in
+//    its main loop (out_prod_narrow_kernel; 1.3-1.5 x the staged kernel);
 //  * the rows are split when that fills the GPU's resident workgroup slots
 //    (sized from the kernel's occupancy) better than the tiles alone; each
 //    split writes its partial tile to the caller's workspace, and a second
@@ -103,8 +107,9 @@ struct FusedArgs {
 // Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
 // it into kWavesI x kWavesJ sub-tiles of MFMA blocks.  kTileI = 64, 128 or
 // 256: 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
-// instruction).  kTileI = 16, for decode-sized m: 1 x 4 waves of 16 x 16
-// blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction).
+// instruction).  kTileI = 16, for decode-sized m on the byte path: 1 x 4
+// waves of 16 x 16 blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction);
+// on the aligned path decode-sized m takes out_prod_narrow_kernel instead.
 template <int kTileI>
 struct Shape {
     static constexpr bool kSmall = kTileI == 16;
@@ -129,10 +134,10 @@ struct Shape {
     // The aligned decode reads both entries of a packed byte at once from a
     // 256-entry table of codebook pairs (one 8-byte LDS read and one byte
     // select per two elements: 11 fewer vector and 4 fewer LDS instructions
-    // per stage; 1-3 % faster at m = 16 and 128).  The 256-row tile leaves it
-    // out: its 2 KiB of LDS would cost that tile a resident workgroup per CU
-    // (2 % slower at m = 512).
-    static constexpr bool kPairTable = kTileI != 256;
+    // per stage; 1-3 % faster at m = 128).  The 256-row tile leaves it out:
+    // its 2 KiB of LDS would cost that tile a resident workgroup per CU (2 %
+    // slower at m = 512); the 16-row tile only runs the byte path.
+    static constexpr bool kPairTable = kTileI == 64 || kTileI == 128;
     // Waves per SIMD the register allocation must allow: the wide tiles'
     // LDS already caps them at 2 (256 rows) and 4 (128 rows) per SIMD, and
     // left alone the compiler spends registers on hoisted LDS addresses until
@@ -252,11 +257,11 @@ __device__ __forceinline__ void load_stage_b(const FusedArgs &a, int64_t k0, int
 // p, element 2p + 1 in its high nibble), all in the block of scale s:
 // v[q] = fl32(codebook4[nibble q] * s).  With the pair table, one 8-byte LDS
 // read returns both entries of a byte.
-template <int kTileI>
+template <bool kPairTable>
 __device__ __forceinline__ void decode8(uint32_t packed4, float s, const float *lds_cb4,
                                         const f32x2 *lds_pair, float (&v)[8])
 {
-    if constexpr (Shape<kTileI>::kPairTable) {
+    if constexpr (kPairTable) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t off = ((packed4 >> (8 * p)) & 0xFFu) << 3;
@@ -310,7 +315,7 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     if (r < k_end && j < a.n_cols) {
         const float s_lo = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
         if constexpr (kAligned8) {
-            decode8<kTileI>(ld.packed4, s_lo, lds_cb4, lds_pair, v);  // one block (see load_stage)
+            decode8<Shape<kTileI>::kPairTable>(ld.packed4, s_lo, lds_cb4, lds_pair, v);  // one block (see load_stage)
         } else {
             const int lb = a.log2_block;
             const int64_t e = r * a.n_cols + j;
@@ -462,7 +467,7 @@ __device__ __forceinline__ void decode_full_stage(const FusedArgs &a, int t,
     const int row = t >> 4, col = (t & 15) * 8;
     const float s = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
     float v[8];
-    decode8<kTileI>(ld.packed4, s, lds_cb4, lds_pair, v);
+    decode8<Shape<kTileI>::kPairTable>(ld.packed4, s, lds_cb4, lds_pair, v);
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         lds_w[row][col + q] = v[q];
@@ -651,6 +656,226 @@ void out_prod_fused_kernel(FusedArgs a)
         }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow tile for decode-sized m (m <= 16) on the aligned path.  With so few
+// dst rows each decoded weight feeds only m products, and staging the weights
+// through LDS (a write and a read per element) made the LDS the limit.  Here
+// each lane decodes its packed dword straight into the operand layout of
+// v_mfma_f32_16x16x4_f32: a step covers 4 weight rows (the instruction's k)
+// and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
+// columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
+// the 8 blocks (block bj's column c is weight column 8c + bj; the store
+// undoes that permutation).  The src1 operand is one float per lane per step,
+// loaded straight from global memory too.  The 4 waves of a workgroup take
+// every fourth step of the split's rows and add their partial tiles at the end
+// in a fixed order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.
+// Only the codebooks live in LDS; the main loop has no barrier.
+constexpr int kNarrowK = 4;       // weight rows per step (n_steps uses >> 2)
+constexpr int kNarrowDepth = 3;   // steps of each wave in flight
+
+struct NarrowLoad {
+    uint32_t packed4;
+    uint32_t code;
+    float absmax;
+    float b;
+    bool valid;   // the step's row for this lane is in the split (checked steps)
+};
+
+template <bool kSrc1Transposed>
+__global__ __launch_bounds__(kThreads) void out_prod_narrow_kernel(FusedArgs a)
+{
+    __shared__ float lds_scb[256];
+    __shared__ f32x2 lds_pair[256];             // (entry of low nibble, high nibble)
+    __shared__ float lds_red[2][32 * 64];       // partial tiles of two waves
+
+    const int t = threadIdx.x;
+    // the wave index is uniform within a wave; saying so keeps the steps'
+    // addresses in scalar registers
+    const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int ti = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.tiles_i));
+    const uint32_t rest = blockIdx.x / static_cast<uint32_t>(a.tiles_i);
+    const int tj = static_cast<int>(rest % static_cast<uint32_t>(a.tiles_j));
+    const int split = static_cast<int>(rest / static_cast<uint32_t>(a.tiles_j));
+    const int64_t i0 = int64_t{ti} * 16, j0 = int64_t{tj} * kTileJ;
+    const int64_t k_begin = int64_t{split} * a.rows_per_split;
+    const int64_t k_end = min(a.n_rows, k_begin + a.rows_per_split);
+
+    lds_scb[t] = a.scale_codebook[t];
+    lds_pair[t] = f32x2{a.codebook4[t & 15], a.codebook4[t >> 4]};
+    __syncthreads();
+
+    // lane constants: row of the step, first of 8 weight columns, src1 column
+    // (lanes past n_cols or m read column j0 or i0: in range, and their
+    // products reach only dst elements that are never stored)
+    const int row = lane >> 4, c = lane & 15;
+    const uint32_t n_cols = static_cast<uint32_t>(a.n_cols);
+    const uint32_t ld_src1 = static_cast<uint32_t>(a.ld);
+    const uint32_t col_in = j0 + 8 * c < a.n_cols ? 8u * c : 0u;
+    const uint32_t w_elem = static_cast<uint32_t>(row) * n_cols + col_in;
+    const uint32_t i_in = i0 + c < a.m ? static_cast<uint32_t>(c) : 0u;
+    const uint32_t b_byte = kSrc1Transposed ? 4u * (i_in * ld_src1 + row)
+                                            : 4u * (row * ld_src1 + i_in);
+    const int lb = a.log2_block;
+
+    const int64_t rows = k_end - k_begin;  // > 0
+    const int n_steps =
+        __builtin_amdgcn_readfirstlane(static_cast<int>((rows + kNarrowK - 1) >> 2));
+    const int n_full =
+        a.full_stages ? __builtin_amdgcn_readfirstlane(static_cast<int>(rows >> 2)) : 0;
+
+    // a full step: uniform bases plus the lane constants, no bounds checks
+    const auto load_full = [&](int s) {
+        NarrowLoad ld;
+        const int64_t k0 = k_begin + int64_t{kNarrowK} * s;
+        const int64_t e0 = k0 * a.n_cols + j0;  // a multiple of 8
+        ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(
+            span_buffer(a.packed + (e0 >> 1), kNarrowK / 2 * n_cols), w_elem >> 1, 0, 0);
+        const int64_t bh = e0 >> lb;
+        const uint32_t bl = static_cast<uint32_t>(e0 & ((int64_t{1} << lb) - 1));
+        const uint32_t cb = (bl + w_elem) >> lb;
+        const uint32_t c_span = ((kNarrowK * n_cols + 4095u) >> lb) + 1u;
+        ld.code = __builtin_amdgcn_raw_buffer_load_b8(span_buffer(a.scale_codes + bh, c_span),
+                                                      cb, 0, 0);
+        const uint32_t g =
+            (static_cast<uint32_t>(bh & ((1 << kNestedLog2) - 1)) + cb) >> kNestedLog2;
+        ld.absmax = load_f32(span_buffer(a.nested_absmax + (bh >> kNestedLog2),
+                                         4u * ((c_span + 255u) / 256u + 1u)),
+                             4u * g);
+        const float *bbase = kSrc1Transposed ? a.src1 + (i0 * a.ld + k0)
+                                             : a.src1 + (k0 * a.ld + i0);
+        ld.b = load_f32(span_buffer(bbase, kSrc1Transposed ? 4u * (16u * ld_src1 + kNarrowK)
+                                                           : 4u * (kNarrowK * ld_src1 + 16u)),
+                        b_byte);
+        ld.valid = true;
+        return ld;
+    };
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int bj = 0; bj < 8; ++bj)
+        acc[bj] = f32x4{};
+    const auto decode = [&](const NarrowLoad &ld, float (&v)[8]) {
+        decode8<true>(ld.packed4, block_scale(lds_scb[ld.code], ld.absmax, a.offset), nullptr,
+                      lds_pair, v);
+    };
+
+    const auto full_step = [&](const NarrowLoad &ld) {
+        float v[8];
+        decode(ld, v);
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+            acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(ld.b, v[bj], acc[bj], 0, 0, 0);
+    };
+    // Full steps: wave w takes steps w, w + 4, w + 8, ... below n_full.  Two
+    // banks of kNarrowDepth loads alternate: the steps of one bank are
+    // computed while the loads of the other fly.  (Written so that no loaded
+    // value is copied between registers -- a copy would wait for the load --
+    // and so that the loop body updates the accumulators unconditionally: a
+    // conditional update keeps the old value live and made the compiler copy
+    // every accumulator on every step.)
+    constexpr int kBank = 4 * kNarrowDepth;  // steps of one bank
+    NarrowLoad bank0[kNarrowDepth], bank1[kNarrowDepth];
+    if (n_full > 0) {
+        // unconditional as in the loop (past n_full: step n_full - 1, unused)
+#pragma unroll
+        for (int d = 0; d < kNarrowDepth; ++d)
+            bank0[d] = load_full(min(wave + 4 * d, n_full - 1));
+#pragma unroll
+        for (int d = 0; d < kNarrowDepth; ++d)
+            bank1[d] = load_full(min(wave + kBank + 4 * d, n_full - 1));
+    }
+    int s0 = wave;  // first step of bank0
+    for (; s0 + kBank + 4 * (kNarrowDepth - 1) < n_full; s0 += 2 * kBank) {
+        // every step of both banks is below n_full
+        // The next loads are issued unconditionally (a step past n_full
+        // reloads step n_full - 1, unused): conditional loads would make the
+        // compiler's count of loads in flight inexact, and it then waits for
+        // all of them.  The scheduling barriers keep each step's loads right
+        // after its use of the registers they refill; left alone, the
+        // scheduler sank all of them to the end of the loop body, where the
+        // next iteration waited for them at once.
+#pragma unroll
+        for (int d = 0; d < kNarrowDepth; ++d) {
+            full_step(bank0[d]);
+            bank0[d] = load_full(min(s0 + 2 * kBank + 4 * d, n_full - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int d = 0; d < kNarrowDepth; ++d) {
+            full_step(bank1[d]);
+            bank1[d] = load_full(min(s0 + 3 * kBank + 4 * d, n_full - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // at most 2 * kNarrowDepth - 1 full steps are left, all loaded
+#pragma unroll
+    for (int d = 0; d < kNarrowDepth; ++d)
+        if (s0 + 4 * d < n_full)
+            full_step(bank0[d]);
+#pragma unroll
+    for (int d = 0; d < kNarrowDepth - 1; ++d)
+        if (s0 + kBank + 4 * d < n_full)
+            full_step(bank1[d]);
+    // the rest (the split's last, partial step; every step when the host
+    // could not allow the full ones): 64-bit indices, both operands of a row
+    // past the split zeroed
+    for (int s = n_full + ((wave - n_full) & 3); s < n_steps; s += 4) {
+        const int64_t r = k_begin + int64_t{kNarrowK} * s + row;
+        NarrowLoad ld{0u, 0u, 0.0f, 0.0f, r < k_end};
+        if (ld.valid) {
+            const int64_t e = r * a.n_cols + j0 + col_in;
+            ld.packed4 = *reinterpret_cast<const uint32_t *>(a.packed + (e >> 1));
+            ld.code = a.scale_codes[e >> lb];
+            ld.absmax = a.nested_absmax[(e >> lb) >> kNestedLog2];
+            ld.b = kSrc1Transposed ? a.src1[(i0 + i_in) * a.ld + r]
+                                   : a.src1[r * a.ld + i0 + i_in];
+        }
+        float v[8];
+        decode(ld, v);
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+            acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(ld.valid ? ld.b : 0.0f,
+                                                           ld.valid ? v[bj] : 0.0f, acc[bj], 0,
+                                                           0, 0);
+    }
+
+    // partial tiles: (w0 + w2) + (w1 + w3); lds_red[x][q * 64 + lane]
+    if (wave >= 2)
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                lds_red[wave - 2][(bj * 4 + v) * 64 + lane] = acc[bj][v];
+    __syncthreads();
+    if (wave < 2)
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[bj][v] = acc[bj][v] + lds_red[wave][(bj * 4 + v) * 64 + lane];
+    __syncthreads();
+    if (wave == 1)
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                lds_red[0][(bj * 4 + v) * 64 + lane] = acc[bj][v];
+    __syncthreads();
+    if (wave != 0 || j0 + 8 * c >= a.n_cols)
+        return;
+    float *out = a.part + int64_t{split} * a.m * a.n_cols;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + 4 * row + v;  // the accumulator's row (see Shape::acc_row)
+        if (i >= a.m)
+            continue;
+        float *o = out + i * a.n_cols + j0 + 8 * c;
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+            o[bj] = acc[bj][v] + lds_red[0][(bj * 4 + v) * 64 + lane];
+    }
+}
+
 // dst[x] = part[0][x] + part[1][x] + ... in split order
 __global__ __launch_bounds__(kThreads) void out_prod_reduce_kernel(const float *part, float *dst,
                                                                    int64_t count, int splits)
@@ -678,8 +903,9 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: 16-row i-tiles for decode-sized m, else the width
-// of least tile_cost.  `variant` (0..15) indexes the instantiation.
+// The kernel for a launch: for decode-sized m the narrow kernel (aligned
+// path) or 16-row i-tiles (byte path), else the width of least tile_cost.
+// `variant` (0..17) indexes the kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -689,7 +915,11 @@ struct Plan {
 template <int kTileI, bool kSrc1Transposed>
 const void *kernel_for(bool aligned8)
 {
-    return aligned8
+    if constexpr (kTileI == 16)  // the aligned path of decode-sized m is the narrow kernel's
+        return reinterpret_cast<const void *>(
+            &out_prod_fused_kernel<16, kSrc1Transposed, false>);
+    else
+        return aligned8
                ? reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, kSrc1Transposed, true>)
                : reinterpret_cast<const void *>(
                      &out_prod_fused_kernel<kTileI, kSrc1Transposed, false>);
@@ -709,9 +939,12 @@ double tile_cost(int64_t m, int64_t tile_i)
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
     const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
+    if (m <= 16 && aligned8)
+        return {transposed ? reinterpret_cast<const void *>(&out_prod_narrow_kernel<true>)
+                           : reinterpret_cast<const void *>(&out_prod_narrow_kernel<false>),
+                16, 16 + (transposed ? 1 : 0)};
     if (m <= 16)
-        return {transposed ? kernel_for<16, true>(aligned8) : kernel_for<16, false>(aligned8),
-                16, sub};
+        return {transposed ? kernel_for<16, true>(false) : kernel_for<16, false>(false), 16, sub};
     int64_t best = 64;
     for (const int64_t w : {128, 256})
         if (tile_cost(m, w) < tile_cost(m, best))
@@ -726,7 +959,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             4 + sub};
 }
 
-constexpr int kVariants = 16;
+constexpr int kVariants = 18;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

@@ -149,6 +149,33 @@ def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
     del flat, wide
 
 
+@pytest.mark.parametrize("transposed", [False, True])
+@pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
+def test_narrow_tile_steps_and_splits(n_rows, transposed):
+    """Decode-sized m on the aligned path takes the narrow tile: 4-row steps
+    spread over the workgroup's 4 waves, its full steps pipelined, the
+    split's last partial step checked, and the waves' partial tiles added at
+    the end.  Row counts below, at and just past a step and a wave round, a
+    ragged last 128-column tile, and every m up to the tile's 16 (with and
+    without row splits): dst row i equals the oracle's weight row sel[i]."""
+    n_cols = 136
+    x = inputs.make_inputs(n_rows * n_cols, 32, "fp4", 0.07, seed=n_rows + 901,
+                           n_rows=n_rows, n_cols=n_cols)
+    dev = dq4.to_device(x)
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    for m in (1, 7, 16):
+        rng = np.random.Generator(np.random.PCG64(n_rows * 17 + m))
+        sel = rng.integers(0, n_rows, size=m)
+        b = np.zeros((n_rows, m), np.float32)
+        b[sel, np.arange(m)] = 1.0
+        for ws in (None, torch.empty(0, device="cuda")):
+            y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
+                                       n_cols=n_cols, blocksize=32, src1=_src1(b, transposed),
+                                       src1_transposed=transposed, workspace=ws).cpu().numpy()
+            bad = np.argwhere(y != w[sel])
+            assert bad.size == 0, f"m={m}: first mismatch at (i, j) = {bad[0]}"
+
+
 def _route(dev, x, n_rows, n_cols, workspace=None):
     def call(**kw):
         return dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
