@@ -44,10 +44,11 @@
 //    bytes whose products land only in dst elements that are never stored),
 //    which halves the vector instructions of a stage (9 % faster at m = 64,
 //    2-11 % at the other widths); the last stage keeps the checked loads;
-//  * decode-sized m (at most 16) on the aligned path takes a narrow kernel
-//    that decodes each packed dword straight into the matrix instruction's
+//  * small m (at most 64) on the aligned path takes a direct kernel that
+//    decodes each packed dword straight into the matrix instruction's
 //    operand registers, with no LDS staging of the weights and no barrier in
-//    its main loop (out_prod_narrow_kernel; 1.3-1.5 x the staged kernel);
+//    its main loop (out_prod_direct_kernel: 1.4 x the staged kernel at
+//    m = 16, 2 x at m = 32, 1.1 x at m = 48, level at m = 64);
 //  * the rows are split when that fills the GPU's resident workgroup slots
 //    (sized from the kernel's occupancy) better than the tiles alone; each
 //    split writes its partial tile to the caller's workspace, and a second
@@ -109,7 +110,7 @@ struct FusedArgs {
 // 256: 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
 // instruction).  kTileI = 16, for decode-sized m on the byte path: 1 x 4
 // waves of 16 x 16 blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction);
-// on the aligned path decode-sized m takes out_prod_narrow_kernel instead.
+// on the aligned path m <= 64 takes out_prod_direct_kernel instead.
 template <int kTileI>
 struct Shape {
     static constexpr bool kSmall = kTileI == 16;
@@ -141,7 +142,7 @@ struct Shape {
     // Waves per SIMD the register allocation must allow: the wide tiles'
     // LDS already caps them at 2 (256 rows) and 4 (128 rows) per SIMD, and
     // left alone the compiler spends registers on hoisted LDS addresses until
-    // fewer fit.  The narrow tiles are left to the compiler.
+    // fewer fit.  The 16- and 64-row tiles are left to the compiler.
     static constexpr int kMinWaves = kTileI == 256 ? 2 : kTileI == 128 ? 4 : 1;
 
     // one MFMA: acc += A (kBlk x kK) x B (kK x kBlk); lane l holds A[l % kBlk][l / kBlk]
@@ -657,36 +658,45 @@ void out_prod_fused_kernel(FusedArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Narrow tile for decode-sized m (m <= 16) on the aligned path.  With so few
-// dst rows each decoded weight feeds only m products, and staging the weights
-// through LDS (a write and a read per element) made the LDS the limit.  Here
-// each lane decodes its packed dword straight into the operand layout of
+// Direct tiles for small m (m <= 64) on the aligned path.  With few dst rows
+// each decoded weight feeds only m products, and staging the weights through
+// LDS (a write and a read per element) made the LDS the limit at m = 16.
+// Here each lane decodes its packed dword straight into the operand layout of
 // v_mfma_f32_16x16x4_f32: a step covers 4 weight rows (the instruction's k)
 // and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
 // columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
-// the 8 blocks (block bj's column c is weight column 8c + bj; the store
-// undoes that permutation).  The src1 operand is one float per lane per step,
-// loaded straight from global memory too.  The 4 waves of a workgroup take
-// every fourth step of the split's rows and add their partial tiles at the end
-// in a fixed order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.
-// Only the codebooks live in LDS; the main loop has no barrier.
-constexpr int kNarrowK = 4;       // weight rows per step (n_steps uses >> 2)
-constexpr int kNarrowDepth = 3;   // steps of each wave in flight
+// the 8 blocks (block bj's column c is weight column 8c + bj).  The tile's
+// 16 * kBI dst rows are kBI blocks of 16 in the same way (block bi's row c is
+// dst row kBI c + bi), so a lane's src1 operands of one step are kBI
+// consecutive floats of one src1 row, loaded straight from global memory.
+// The store undoes both permutations.  The 4 waves of a workgroup take every
+// fourth step of the split's rows and add their partial tiles at the end in a
+// fixed order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.
+// Only the codebooks live in LDS during the main loop, which has no barrier.
+constexpr int kDirectK = 4;   // weight rows per step (n_steps uses >> 2)
 
-struct NarrowLoad {
+template <int kBI>
+struct DirectLoad {
     uint32_t packed4;
     uint32_t code;
     float absmax;
-    float b;
-    bool valid;   // the step's row for this lane is in the split (checked steps)
+    float b[kBI];
 };
 
-template <bool kSrc1Transposed>
-__global__ __launch_bounds__(kThreads) void out_prod_narrow_kernel(FusedArgs a)
+template <int kBI>
+struct Direct {
+    static constexpr int kRows = 16 * kBI;          // dst rows of the tile
+    static constexpr int kDepth = kBI == 4 ? 2 : 3; // steps per register bank
+    static constexpr int kMinWaves = kBI == 4 ? 2 : 1;
+};
+
+template <int kBI, bool kSrc1Transposed>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Direct<kBI>::kMinWaves)))
+void out_prod_direct_kernel(FusedArgs a)
 {
     __shared__ float lds_scb[256];
-    __shared__ f32x2 lds_pair[256];             // (entry of low nibble, high nibble)
-    __shared__ float lds_red[2][32 * 64];       // partial tiles of two waves
+    __shared__ f32x2 lds_pair[256];                  // (entry of low nibble, high nibble)
+    __shared__ float lds_red[2][kBI * 32 * 64];      // partial tiles of two waves
 
     const int t = threadIdx.x;
     // the wave index is uniform within a wave; saying so keeps the steps'
@@ -696,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void out_prod_narrow_kernel(FusedArgs a)
     const uint32_t rest = blockIdx.x / static_cast<uint32_t>(a.tiles_i);
     const int tj = static_cast<int>(rest % static_cast<uint32_t>(a.tiles_j));
     const int split = static_cast<int>(rest / static_cast<uint32_t>(a.tiles_j));
-    const int64_t i0 = int64_t{ti} * 16, j0 = int64_t{tj} * kTileJ;
+    const int64_t i0 = int64_t{ti} * Direct<kBI>::kRows, j0 = int64_t{tj} * kTileJ;
     const int64_t k_begin = int64_t{split} * a.rows_per_split;
     const int64_t k_end = min(a.n_rows, k_begin + a.rows_per_split);
 
@@ -704,36 +714,41 @@ __global__ __launch_bounds__(kThreads) void out_prod_narrow_kernel(FusedArgs a)
     lds_pair[t] = f32x2{a.codebook4[t & 15], a.codebook4[t >> 4]};
     __syncthreads();
 
-    // lane constants: row of the step, first of 8 weight columns, src1 column
-    // (lanes past n_cols or m read column j0 or i0: in range, and their
-    // products reach only dst elements that are never stored)
+    // lane constants: row of the step, first of 8 weight columns, src1
+    // columns (lanes past n_cols read column j0, and src1 columns past m read
+    // column m - 1: in range, and their products reach only dst elements that
+    // are never stored)
     const int row = lane >> 4, c = lane & 15;
     const uint32_t n_cols = static_cast<uint32_t>(a.n_cols);
     const uint32_t ld_src1 = static_cast<uint32_t>(a.ld);
     const uint32_t col_in = j0 + 8 * c < a.n_cols ? 8u * c : 0u;
     const uint32_t w_elem = static_cast<uint32_t>(row) * n_cols + col_in;
-    const uint32_t i_in = i0 + c < a.m ? static_cast<uint32_t>(c) : 0u;
-    const uint32_t b_byte = kSrc1Transposed ? 4u * (i_in * ld_src1 + row)
-                                            : 4u * (row * ld_src1 + i_in);
+    const uint32_t i_last = static_cast<uint32_t>(min(a.m - i0, int64_t{Direct<kBI>::kRows}) - 1);
+    uint32_t b_off[kBI];  // bytes from the step's first src1 element
+#pragma unroll
+    for (int bi = 0; bi < kBI; ++bi) {
+        const uint32_t il = min(static_cast<uint32_t>(kBI * c + bi), i_last);
+        b_off[bi] = kSrc1Transposed ? 4u * (il * ld_src1 + row) : 4u * (row * ld_src1 + il);
+    }
     const int lb = a.log2_block;
 
     const int64_t rows = k_end - k_begin;  // > 0
     const int n_steps =
-        __builtin_amdgcn_readfirstlane(static_cast<int>((rows + kNarrowK - 1) >> 2));
+        __builtin_amdgcn_readfirstlane(static_cast<int>((rows + kDirectK - 1) >> 2));
     const int n_full =
         a.full_stages ? __builtin_amdgcn_readfirstlane(static_cast<int>(rows >> 2)) : 0;
 
     // a full step: uniform bases plus the lane constants, no bounds checks
     const auto load_full = [&](int s) {
-        NarrowLoad ld;
-        const int64_t k0 = k_begin + int64_t{kNarrowK} * s;
+        DirectLoad<kBI> ld;
+        const int64_t k0 = k_begin + int64_t{kDirectK} * s;
         const int64_t e0 = k0 * a.n_cols + j0;  // a multiple of 8
         ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(
-            span_buffer(a.packed + (e0 >> 1), kNarrowK / 2 * n_cols), w_elem >> 1, 0, 0);
+            span_buffer(a.packed + (e0 >> 1), kDirectK / 2 * n_cols), w_elem >> 1, 0, 0);
         const int64_t bh = e0 >> lb;
         const uint32_t bl = static_cast<uint32_t>(e0 & ((int64_t{1} << lb) - 1));
         const uint32_t cb = (bl + w_elem) >> lb;
-        const uint32_t c_span = ((kNarrowK * n_cols + 4095u) >> lb) + 1u;
+        const uint32_t c_span = ((kDirectK * n_cols + 4095u) >> lb) + 1u;
         ld.code = __builtin_amdgcn_raw_buffer_load_b8(span_buffer(a.scale_codes + bh, c_span),
                                                       cb, 0, 0);
         const uint32_t g =
@@ -741,139 +756,176 @@ __global__ __launch_bounds__(kThreads) void out_prod_narrow_kernel(FusedArgs a)
         ld.absmax = load_f32(span_buffer(a.nested_absmax + (bh >> kNestedLog2),
                                          4u * ((c_span + 255u) / 256u + 1u)),
                              4u * g);
-        const float *bbase = kSrc1Transposed ? a.src1 + (i0 * a.ld + k0)
-                                             : a.src1 + (k0 * a.ld + i0);
-        ld.b = load_f32(span_buffer(bbase, kSrc1Transposed ? 4u * (16u * ld_src1 + kNarrowK)
-                                                           : 4u * (kNarrowK * ld_src1 + 16u)),
-                        b_byte);
-        ld.valid = true;
+        const __amdgpu_buffer_rsrc_t b =
+            kSrc1Transposed
+                ? span_buffer(a.src1 + (i0 * a.ld + k0),
+                              4u * (Direct<kBI>::kRows * ld_src1 + kDirectK))
+                : span_buffer(a.src1 + (k0 * a.ld + i0),
+                              4u * (kDirectK * ld_src1 + Direct<kBI>::kRows));
+#pragma unroll
+        for (int bi = 0; bi < kBI; ++bi)
+            ld.b[bi] = load_f32(b, b_off[bi]);
         return ld;
     };
 
-    f32x4 acc[8];
+    f32x4 acc[kBI][8];
 #pragma unroll
-    for (int bj = 0; bj < 8; ++bj)
-        acc[bj] = f32x4{};
-    const auto decode = [&](const NarrowLoad &ld, float (&v)[8]) {
+    for (int bi = 0; bi < kBI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+            acc[bi][bj] = f32x4{};
+    const auto decode = [&](const DirectLoad<kBI> &ld, float (&v)[8]) {
         decode8<true>(ld.packed4, block_scale(lds_scb[ld.code], ld.absmax, a.offset), nullptr,
                       lds_pair, v);
     };
-
-    const auto full_step = [&](const NarrowLoad &ld) {
+    const auto full_step = [&](const DirectLoad<kBI> &ld) {
         float v[8];
         decode(ld, v);
 #pragma unroll
         for (int bj = 0; bj < 8; ++bj)
-            acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(ld.b, v[bj], acc[bj], 0, 0, 0);
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                acc[bi][bj] =
+                    __builtin_amdgcn_mfma_f32_16x16x4f32(ld.b[bi], v[bj], acc[bi][bj], 0, 0, 0);
     };
+    // a loaded step that may lie past n_full: its operands zeroed there, so
+    // that the accumulators are updated unconditionally (see below)
+    const auto masked_step = [&](const DirectLoad<kBI> &ld, bool use) {
+        float v[8];
+        decode(ld, v);
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    use ? ld.b[bi] : 0.0f, use ? v[bj] : 0.0f, acc[bi][bj], 0, 0, 0);
+    };
+
     // Full steps: wave w takes steps w, w + 4, w + 8, ... below n_full.  Two
-    // banks of kNarrowDepth loads alternate: the steps of one bank are
-    // computed while the loads of the other fly.  (Written so that no loaded
-    // value is copied between registers -- a copy would wait for the load --
-    // and so that the loop body updates the accumulators unconditionally: a
+    // banks of kDepth loads alternate: the steps of one bank are computed
+    // while the loads of the other fly.  (Written so that no loaded value is
+    // copied between registers -- a copy would wait for the load -- and so
+    // that the loop body updates the accumulators unconditionally: a
     // conditional update keeps the old value live and made the compiler copy
     // every accumulator on every step.)
-    constexpr int kBank = 4 * kNarrowDepth;  // steps of one bank
-    NarrowLoad bank0[kNarrowDepth], bank1[kNarrowDepth];
+    constexpr int kDepth = Direct<kBI>::kDepth;
+    constexpr int kBank = 4 * kDepth;  // steps of one bank
+    DirectLoad<kBI> bank0[kDepth], bank1[kDepth];
     if (n_full > 0) {
         // unconditional as in the loop (past n_full: step n_full - 1, unused)
 #pragma unroll
-        for (int d = 0; d < kNarrowDepth; ++d)
+        for (int d = 0; d < kDepth; ++d)
             bank0[d] = load_full(min(wave + 4 * d, n_full - 1));
 #pragma unroll
-        for (int d = 0; d < kNarrowDepth; ++d)
+        for (int d = 0; d < kDepth; ++d)
             bank1[d] = load_full(min(wave + kBank + 4 * d, n_full - 1));
     }
     int s0 = wave;  // first step of bank0
-    for (; s0 + kBank + 4 * (kNarrowDepth - 1) < n_full; s0 += 2 * kBank) {
-        // every step of both banks is below n_full
-        // The next loads are issued unconditionally (a step past n_full
-        // reloads step n_full - 1, unused): conditional loads would make the
-        // compiler's count of loads in flight inexact, and it then waits for
-        // all of them.  The scheduling barriers keep each step's loads right
-        // after its use of the registers they refill; left alone, the
-        // scheduler sank all of them to the end of the loop body, where the
-        // next iteration waited for them at once.
+    for (; s0 + kBank + 4 * (kDepth - 1) < n_full; s0 += 2 * kBank) {
+        // Every step of both banks is below n_full.  The next loads are
+        // issued unconditionally (a step past n_full reloads step n_full - 1,
+        // unused): conditional loads would make the compiler's count of loads
+        // in flight inexact, and it then waits for all of them.  The
+        // scheduling barriers keep each step's loads right after its use of
+        // the registers they refill; left alone, the scheduler sank all of
+        // them to the end of the loop body, where the next iteration waited
+        // for them at once.
 #pragma unroll
-        for (int d = 0; d < kNarrowDepth; ++d) {
+        for (int d = 0; d < kDepth; ++d) {
             full_step(bank0[d]);
             bank0[d] = load_full(min(s0 + 2 * kBank + 4 * d, n_full - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int d = 0; d < kNarrowDepth; ++d) {
+        for (int d = 0; d < kDepth; ++d) {
             full_step(bank1[d]);
             bank1[d] = load_full(min(s0 + 3 * kBank + 4 * d, n_full - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // at most 2 * kNarrowDepth - 1 full steps are left, all loaded
+    // at most 2 * kDepth - 1 full steps are left, all loaded
+    if (n_full > 0) {
 #pragma unroll
-    for (int d = 0; d < kNarrowDepth; ++d)
-        if (s0 + 4 * d < n_full)
-            full_step(bank0[d]);
+        for (int d = 0; d < kDepth; ++d)
+            masked_step(bank0[d], s0 + 4 * d < n_full);
 #pragma unroll
-    for (int d = 0; d < kNarrowDepth - 1; ++d)
-        if (s0 + kBank + 4 * d < n_full)
-            full_step(bank1[d]);
+        for (int d = 0; d < kDepth - 1; ++d)
+            masked_step(bank1[d], s0 + kBank + 4 * d < n_full);
+    }
     // the rest (the split's last, partial step; every step when the host
     // could not allow the full ones): 64-bit indices, both operands of a row
     // past the split zeroed
     for (int s = n_full + ((wave - n_full) & 3); s < n_steps; s += 4) {
-        const int64_t r = k_begin + int64_t{kNarrowK} * s + row;
-        NarrowLoad ld{0u, 0u, 0.0f, 0.0f, r < k_end};
-        if (ld.valid) {
+        const int64_t r = k_begin + int64_t{kDirectK} * s + row;
+        const bool valid = r < k_end;
+        DirectLoad<kBI> ld{};
+        if (valid) {
             const int64_t e = r * a.n_cols + j0 + col_in;
             ld.packed4 = *reinterpret_cast<const uint32_t *>(a.packed + (e >> 1));
             ld.code = a.scale_codes[e >> lb];
             ld.absmax = a.nested_absmax[(e >> lb) >> kNestedLog2];
-            ld.b = kSrc1Transposed ? a.src1[(i0 + i_in) * a.ld + r]
-                                   : a.src1[r * a.ld + i0 + i_in];
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi) {
+                const int64_t i = i0 + min(static_cast<uint32_t>(kBI * c + bi), i_last);
+                ld.b[bi] = kSrc1Transposed ? a.src1[i * a.ld + r] : a.src1[r * a.ld + i];
+            }
         }
         float v[8];
         decode(ld, v);
 #pragma unroll
         for (int bj = 0; bj < 8; ++bj)
-            acc[bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(ld.valid ? ld.b : 0.0f,
-                                                           ld.valid ? v[bj] : 0.0f, acc[bj], 0,
-                                                           0, 0);
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    valid ? ld.b[bi] : 0.0f, valid ? v[bj] : 0.0f, acc[bi][bj], 0, 0, 0);
     }
 
-    // partial tiles: (w0 + w2) + (w1 + w3); lds_red[x][q * 64 + lane]
+    // partial tiles: (w0 + w2) + (w1 + w3); lds_red[x][q * 64 + lane] with
+    // q = (bi * 8 + bj) * 4 + v
     if (wave >= 2)
 #pragma unroll
-        for (int bj = 0; bj < 8; ++bj)
+        for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                lds_red[wave - 2][(bj * 4 + v) * 64 + lane] = acc[bj][v];
+            for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    lds_red[wave - 2][((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
     __syncthreads();
     if (wave < 2)
 #pragma unroll
-        for (int bj = 0; bj < 8; ++bj)
+        for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                acc[bj][v] = acc[bj][v] + lds_red[wave][(bj * 4 + v) * 64 + lane];
+            for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[bi][bj][v] =
+                        acc[bi][bj][v] + lds_red[wave][((bi * 8 + bj) * 4 + v) * 64 + lane];
     __syncthreads();
     if (wave == 1)
 #pragma unroll
-        for (int bj = 0; bj < 8; ++bj)
+        for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                lds_red[0][(bj * 4 + v) * 64 + lane] = acc[bj][v];
+            for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    lds_red[0][((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
     __syncthreads();
     if (wave != 0 || j0 + 8 * c >= a.n_cols)
         return;
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int64_t i = i0 + 4 * row + v;  // the accumulator's row (see Shape::acc_row)
-        if (i >= a.m)
-            continue;
-        float *o = out + i * a.n_cols + j0 + 8 * c;
+    for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 8; ++bj)
-            o[bj] = acc[bj][v] + lds_red[0][(bj * 4 + v) * 64 + lane];
-    }
+        for (int v = 0; v < 4; ++v) {
+            // the accumulator's row 4 * row + v (see Shape::acc_row) of block bi
+            const int64_t i = i0 + kBI * (4 * row + v) + bi;
+            if (i >= a.m)
+                continue;
+            float *o = out + i * a.n_cols + j0 + 8 * c;
+#pragma unroll
+            for (int bj = 0; bj < 8; ++bj)
+                o[bj] = acc[bi][bj][v] + lds_red[0][((bi * 8 + bj) * 4 + v) * 64 + lane];
+        }
 }
 
 // dst[x] = part[0][x] + part[1][x] + ... in split order
@@ -903,9 +955,10 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: for decode-sized m the narrow kernel (aligned
-// path) or 16-row i-tiles (byte path), else the width of least tile_cost.
-// `variant` (0..17) indexes the kernel for the occupancy cache.
+// The kernel for a launch: on the aligned path the direct kernel for m <= 64
+// (16, 32 or 64 rows per tile); 16-row tiles for decode-sized m on the byte
+// path; else the width of least tile_cost.
+// `variant` (0..21) indexes the kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -915,7 +968,7 @@ struct Plan {
 template <int kTileI, bool kSrc1Transposed>
 const void *kernel_for(bool aligned8)
 {
-    if constexpr (kTileI == 16)  // the aligned path of decode-sized m is the narrow kernel's
+    if constexpr (kTileI == 16)  // the aligned path of m <= 64 is the direct kernel's
         return reinterpret_cast<const void *>(
             &out_prod_fused_kernel<16, kSrc1Transposed, false>);
     else
@@ -936,13 +989,24 @@ double tile_cost(int64_t m, int64_t tile_i)
     return static_cast<double>(ceil_div(m, tile_i) * tile_i) * rel;
 }
 
+template <int kBI>
+const void *direct_kernel(bool transposed)
+{
+    return transposed ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, true>)
+                      : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, false>);
+}
+
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
     const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
-    if (m <= 16 && aligned8)
-        return {transposed ? reinterpret_cast<const void *>(&out_prod_narrow_kernel<true>)
-                           : reinterpret_cast<const void *>(&out_prod_narrow_kernel<false>),
-                16, 16 + (transposed ? 1 : 0)};
+    if (m <= 64 && aligned8) {
+        const int t = transposed ? 1 : 0;
+        if (m <= 16)
+            return {direct_kernel<1>(transposed), 16, 16 + t};
+        if (m <= 32)
+            return {direct_kernel<2>(transposed), 32, 18 + t};
+        return {direct_kernel<4>(transposed), 64, 20 + t};
+    }
     if (m <= 16)
         return {transposed ? kernel_for<16, true>(false) : kernel_for<16, false>(false), 16, sub};
     int64_t best = 64;
@@ -959,7 +1023,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             4 + sub};
 }
 
-constexpr int kVariants = 18;
+constexpr int kVariants = 22;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

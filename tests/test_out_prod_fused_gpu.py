@@ -151,19 +151,21 @@ def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
 
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
-def test_narrow_tile_steps_and_splits(n_rows, transposed):
-    """Decode-sized m on the aligned path takes the narrow tile: 4-row steps
-    spread over the workgroup's 4 waves, its full steps pipelined, the
-    split's last partial step checked, and the waves' partial tiles added at
-    the end.  Row counts below, at and just past a step and a wave round, a
-    ragged last 128-column tile, and every m up to the tile's 16 (with and
-    without row splits): dst row i equals the oracle's weight row sel[i]."""
+def test_direct_tiles_steps_and_splits(n_rows, transposed):
+    """m <= 64 on the aligned path takes the direct kernel (16, 32 or 64 dst
+    rows per tile, the rows permuted within the tile): 4-row steps spread
+    over the workgroup's 4 waves, its full steps pipelined, the split's last
+    partial step checked, and the waves' partial tiles added at the end.  Row
+    counts below, at and just past a step and a wave round, a ragged last
+    128-column tile, and m at and past each tile width and ragged within it
+    (with and without row splits): dst row i equals the oracle's weight row
+    sel[i]."""
     n_cols = 136
     x = inputs.make_inputs(n_rows * n_cols, 32, "fp4", 0.07, seed=n_rows + 901,
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
-    for m in (1, 7, 16):
+    for m in (1, 7, 16, 17, 32, 45, 64):
         rng = np.random.Generator(np.random.PCG64(n_rows * 17 + m))
         sel = rng.integers(0, n_rows, size=m)
         b = np.zeros((n_rows, m), np.float32)
