@@ -928,7 +928,12 @@ void out_prod_direct_kernel(FusedArgs a)
         }
 }
 
-// dst[x] = part[0][x] + part[1][x] + ... in split order
+// dst[x] = part[0][x] + part[1][x] + ... in split order.  Each thread loads
+// kReduceBatch partials before adding them in order, so that the loads
+// overlap (one at a time, the call was bound by their latency: 14 us for 36
+// splits of a 16 x 5376 dst); the sum is the plain loop's.
+constexpr int kReduceBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void out_prod_reduce_kernel(const float *part, float *dst,
                                                                    int64_t count, int splits)
 {
@@ -936,7 +941,17 @@ __global__ __launch_bounds__(kThreads) void out_prod_reduce_kernel(const float *
     for (int64_t x = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; x < count;
          x += stride) {
         float sum = part[x];
-        for (int s = 1; s < splits; ++s)
+        int s = 1;
+        for (; s + kReduceBatch <= splits; s += kReduceBatch) {
+            float v[kReduceBatch];
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q)
+                v[q] = part[int64_t{s + q} * count + x];
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q)
+                sum = sum + v[q];
+        }
+        for (; s < splits; ++s)
             sum = sum + part[int64_t{s} * count + x];
         dst[x] = sum;
     }
