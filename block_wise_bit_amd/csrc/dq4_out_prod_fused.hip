@@ -48,7 +48,7 @@
 //    decodes each packed dword straight into the matrix instruction's
 //    operand registers, with no LDS staging of the weights and no barrier in
 //    its main loop (out_prod_direct_kernel: 1.4 x the staged kernel at
-//    m = 16, 2 x at m = 32, 1.1 x at m = 48, level at m = 64);
+//    m = 16, 2 x at m = 32, 1.3 x at m = 48, level at m = 64);
 //  * the rows are split when that fills the GPU's resident workgroup slots
 //    (sized from the kernel's occupancy) better than the tiles alone; each
 //    split writes its partial tile to the caller's workspace, and a second
@@ -666,7 +666,7 @@ void out_prod_fused_kernel(FusedArgs a)
 // and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
 // columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
 // the 8 blocks (block bj's column c is weight column 8c + bj).  The tile's
-// 16 * kBI dst rows are kBI blocks of 16 in the same way (block bi's row c is
+// 16 * kBI dst rows (kBI = 1 .. 4) are kBI blocks of 16 in the same way (block bi's row c is
 // dst row kBI c + bi), so a lane's src1 operands of one step are kBI
 // consecutive floats of one src1 row, loaded straight from global memory.
 // The store undoes both permutations.  The 4 waves of a workgroup take every
@@ -686,8 +686,8 @@ struct DirectLoad {
 template <int kBI>
 struct Direct {
     static constexpr int kRows = 16 * kBI;          // dst rows of the tile
-    static constexpr int kDepth = kBI == 4 ? 2 : 3; // steps per register bank
-    static constexpr int kMinWaves = kBI == 4 ? 2 : 1;
+    static constexpr int kDepth = kBI >= 3 ? 2 : 3; // steps per register bank
+    static constexpr int kMinWaves = kBI >= 3 ? 2 : 1;
 };
 
 template <int kBI, bool kSrc1Transposed>
@@ -971,9 +971,9 @@ int64_t ceil_div(int64_t a, int64_t b)
 }
 
 // The kernel for a launch: on the aligned path the direct kernel for m <= 64
-// (16, 32 or 64 rows per tile); 16-row tiles for decode-sized m on the byte
-// path; else the width of least tile_cost.
-// `variant` (0..21) indexes the kernel for the occupancy cache.
+// (16, 32, 48 or 64 rows per tile); 16-row tiles for decode-sized m on the
+// byte path; else the width of least tile_cost.
+// `variant` (0..23) indexes the kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -1020,6 +1020,8 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             return {direct_kernel<1>(transposed), 16, 16 + t};
         if (m <= 32)
             return {direct_kernel<2>(transposed), 32, 18 + t};
+        if (m <= 48)
+            return {direct_kernel<3>(transposed), 48, 22 + t};
         return {direct_kernel<4>(transposed), 64, 20 + t};
     }
     if (m <= 16)
@@ -1038,7 +1040,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             4 + sub};
 }
 
-constexpr int kVariants = 22;
+constexpr int kVariants = 24;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

@@ -152,8 +152,8 @@ def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
 def test_direct_tiles_steps_and_splits(n_rows, transposed):
-    """m <= 64 on the aligned path takes the direct kernel (16, 32 or 64 dst
-    rows per tile, the rows permuted within the tile): 4-row steps spread
+    """m <= 64 on the aligned path takes the direct kernel (16, 32, 48 or 64
+    dst rows per tile, the rows permuted within the tile): 4-row steps spread
     over the workgroup's 4 waves, its full steps pipelined, the split's last
     partial step checked, and the waves' partial tiles added at the end.  Row
     counts below, at and just past a step and a wave round, a ragged last
@@ -165,7 +165,7 @@ def test_direct_tiles_steps_and_splits(n_rows, transposed):
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
-    for m in (1, 7, 16, 17, 32, 45, 64):
+    for m in (1, 7, 16, 17, 32, 33, 45, 48, 49, 64):
         rng = np.random.Generator(np.random.PCG64(n_rows * 17 + m))
         sel = rng.integers(0, n_rows, size=m)
         b = np.zeros((n_rows, m), np.float32)
