@@ -686,7 +686,6 @@ struct DirectLoad {
 template <int kBI>
 struct Direct {
     static constexpr int kRows = 16 * kBI;          // dst rows of the tile
-    static constexpr int kDepth = kBI >= 3 ? 2 : 3; // steps per register bank
     static constexpr int kMinWaves = kBI >= 3 ? 2 : 1;
 };
 
@@ -696,7 +695,7 @@ void out_prod_direct_kernel(FusedArgs a)
 {
     __shared__ float lds_scb[256];
     __shared__ f32x2 lds_pair[256];                  // (entry of low nibble, high nibble)
-    __shared__ float lds_red[2][kBI * 32 * 64];      // partial tiles of two waves
+    __shared__ float lds_red[kBI * 32 * 64];         // a wave's partial tile
 
     const int t = threadIdx.x;
     // the wave index is uniform within a wave; saying so keeps the steps'
@@ -808,7 +807,10 @@ void out_prod_direct_kernel(FusedArgs a)
     // that the loop body updates the accumulators unconditionally: a
     // conditional update keeps the old value live and made the compiler copy
     // every accumulator on every step.)
-    constexpr int kDepth = Direct<kBI>::kDepth;
+    // steps per register bank: at kBI >= 3 one step for a row-major src1
+    // (fewer registers, 3 % faster at m = 48 and 64), two for a transposed
+    // one, whose kBI loads per step are kBI separate rows (3 % slower with one)
+    constexpr int kDepth = kBI >= 3 ? (kSrc1Transposed ? 2 : 1) : 3;
     constexpr int kBank = 4 * kDepth;  // steps of one bank
     DirectLoad<kBI> bank0[kDepth], bank1[kDepth];
     if (n_full > 0) {
@@ -880,35 +882,41 @@ void out_prod_direct_kernel(FusedArgs a)
                     valid ? ld.b[bi] : 0.0f, valid ? v[bj] : 0.0f, acc[bi][bj], 0, 0, 0);
     }
 
-    // partial tiles: (w0 + w2) + (w1 + w3); lds_red[x][q * 64 + lane] with
-    // q = (bi * 8 + bj) * 4 + v
-    if (wave >= 2)
+    // partial tiles: (w0 + w2) + (w1 + w3), through one LDS buffer in three
+    // rounds (a buffer per pair of waves would double the kernel's LDS and
+    // cost resident workgroups); lds_red[q * 64 + lane], q = (bi * 8 + bj) * 4 + v
+    const auto put = [&]() {
 #pragma unroll
         for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    lds_red[wave - 2][((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
+                    lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
+    };
+    const auto add = [&]() {
+#pragma unroll
+        for (int bi = 0; bi < kBI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[bi][bj][v] = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
+    };
+    if (wave == 2)
+        put();
     __syncthreads();
-    if (wave < 2)
-#pragma unroll
-        for (int bi = 0; bi < kBI; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 8; ++bj)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[bi][bj][v] =
-                        acc[bi][bj][v] + lds_red[wave][((bi * 8 + bj) * 4 + v) * 64 + lane];
+    if (wave == 0)
+        add();  // w0 + w2
+    __syncthreads();
+    if (wave == 3)
+        put();
     __syncthreads();
     if (wave == 1)
-#pragma unroll
-        for (int bi = 0; bi < kBI; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 8; ++bj)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    lds_red[0][((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
+        add();  // w1 + w3
+    __syncthreads();
+    if (wave == 1)
+        put();
     __syncthreads();
     if (wave != 0 || j0 + 8 * c >= a.n_cols)
         return;
@@ -924,7 +932,7 @@ void out_prod_direct_kernel(FusedArgs a)
             float *o = out + i * a.n_cols + j0 + 8 * c;
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
-                o[bj] = acc[bi][bj][v] + lds_red[0][((bi * 8 + bj) * 4 + v) * 64 + lane];
+                o[bj] = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
         }
 }
 
