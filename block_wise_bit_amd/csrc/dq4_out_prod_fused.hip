@@ -666,13 +666,14 @@ void out_prod_fused_kernel(FusedArgs a)
 // and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
 // columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
 // the 8 blocks (block bj's column c is weight column 8c + bj).  The tile's
-// 16 * kBI dst rows (kBI = 1 .. 4) are kBI blocks of 16 in the same way (block bi's row c is
-// dst row kBI c + bi), so a lane's src1 operands of one step are kBI
-// consecutive floats of one src1 row, loaded straight from global memory.
-// The store undoes both permutations.  The 4 waves of a workgroup take every
-// fourth step of the split's rows and add their partial tiles at the end in a
-// fixed order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.
-// Only the codebooks live in LDS during the main loop, which has no barrier.
+// 16 * kBI dst rows (kBI = 1 .. 4) are kBI blocks of 16 in the same way
+// (block bi's row c is dst row kBI c + bi), so a lane's src1 operands of one
+// step are kBI consecutive floats of one src1 row, loaded straight from
+// global memory.  The store undoes both permutations.  The 4 waves of a
+// workgroup take every fourth step of the split's rows and add their partial
+// tiles at the end in a fixed order ((w0 + w2) + (w1 + w3)), so the result
+// stays deterministic.  Only the codebooks live in LDS during the main loop,
+// which has no barrier.
 constexpr int kDirectK = 4;   // weight rows per step (n_steps uses >> 2)
 
 template <int kBI>
