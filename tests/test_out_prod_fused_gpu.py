@@ -178,6 +178,33 @@ def test_direct_tiles_steps_and_splits(n_rows, transposed):
             assert bad.size == 0, f"m={m}: first mismatch at (i, j) = {bad[0]}"
 
 
+def test_staged_tile_keeps_checked_loads_past_32_bit_offsets():
+    """The staged kernel's counterpart of the test above: m = 65 takes the
+    128-row staged tile, and a transposed src1 whose leading dimension puts
+    the tile's 128 columns more than 2^32 bytes apart keeps every stage on
+    the checked loads.  Bits equal those of a compact src1, and the rows are
+    the oracle's."""
+    n_rows, n_cols, m = 16 + 5, 256, 65
+    ld = (1 << 23) + 16
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.01, seed=779, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    sel = np.arange(m) % n_rows
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    flat = torch.full(((m - 1) * ld + n_rows,), float("nan"), device="cuda")
+    wide = flat.as_strided((m, n_rows), (ld, 1))
+    wide.copy_(_src1(b, True))
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64,
+              src1_transposed=True)
+    y_wide = dq4.dq4_out_prod_fused(**dev, **kw, src1=wide).cpu().numpy()
+    y_compact = dq4.dq4_out_prod_fused(**dev, **kw, src1=_src1(b, True)).cpu().numpy()
+    assert np.array_equal(y_wide.view(np.uint32), y_compact.view(np.uint32))
+    assert np.array_equal(y_wide, w[sel])
+    del flat, wide
+
+
 def _route(dev, x, n_rows, n_cols, workspace=None):
     def call(**kw):
         return dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
