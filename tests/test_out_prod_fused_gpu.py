@@ -249,11 +249,12 @@ def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
                                           f"workspace={'preferred' if ws is None else 'none'}")
 
 
-@pytest.mark.parametrize("m", [16, 64, 512])
+@pytest.mark.parametrize("m", [16, 32, 48, 64, 512])
 def test_selection_output_head_is_bit_exact(m):
     """Selection-matrix src1 over the 151 936 x 5 376 output head, both
-    orientations, at each i-tile width (16, 64 and 256 rows): every row split
-    is selected; dst equals the weight rows exactly."""
+    orientations, at each tile of the direct kernel (16, 32, 48 and 64 rows)
+    and the staged 256-row tile: every row split is selected; dst equals the
+    weight rows exactly."""
     wl = inputs.OUTPUT_HEAD
     x = cases.output_head_weight()
     dev = dq4.to_device(x)
