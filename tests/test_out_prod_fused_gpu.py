@@ -31,7 +31,7 @@ import block_wise_bit_amd as dq4
 from block_wise_bit_amd import inputs
 import out_prod_cases as cases
 from gpu_util import (check_selection_route, check_sum_bound, oracle_bits, out_prod_reference,
-                      say)
+                      say, weight_rows)
 
 torch = pytest.importorskip("torch")
 
@@ -203,6 +203,38 @@ def test_staged_tile_keeps_checked_loads_past_32_bit_offsets():
     assert np.array_equal(y_wide.view(np.uint32), y_compact.view(np.uint32))
     assert np.array_equal(y_wide, w[sel])
     del flat, wide
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+@pytest.mark.parametrize("m", [16, 48, 100])
+def test_infinite_src1_reaches_only_its_own_products(m, transposed):
+    """An infinity in src1 must reach exactly the dst elements the sum gives
+    it: each workgroup reads only the rows of its own split, and zeroes both
+    operands of the rows that pad its last step, so no inf * 0 = NaN shows up
+    elsewhere.  One +inf per src1 column at a random row (the rows cover many
+    splits); the NaN and infinity pattern of dst, and the infinities' signs,
+    equal those of inf * W[r][j] added to the finite part, and every other
+    element is finite (direct tiles at m = 16 and 48, the staged tile at
+    m = 100)."""
+    n_rows, n_cols = 4099, 384
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=780 + m, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(m))
+    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    r_inf = rng.integers(0, n_rows, size=m)
+    b[r_inf, np.arange(m)] = np.inf
+    y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                               blocksize=64, src1=_src1(b, transposed),
+                               src1_transposed=transposed).cpu().numpy()
+    w_inf = weight_rows(x, n_cols, r_inf).astype(np.float64)   # row i: W[r_inf[i]]
+    with np.errstate(invalid="ignore"):
+        want = np.inf * w_inf            # +-inf, or NaN where the weight is 0
+    assert np.array_equal(np.isnan(y), np.isnan(want)), "NaN pattern"
+    assert np.array_equal(np.isinf(y), np.isinf(want)), "infinity pattern"
+    inf = np.isinf(want)
+    assert np.array_equal(np.sign(y[inf]), np.sign(want[inf])), "infinity signs"
+    assert np.isfinite(y[np.isfinite(want)]).all()
 
 
 def _route(dev, x, n_rows, n_cols, workspace=None):
