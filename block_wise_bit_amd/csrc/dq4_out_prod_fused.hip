@@ -674,6 +674,20 @@ void out_prod_fused_kernel(FusedArgs a)
 // tiles at the end in a fixed order ((w0 + w2) + (w1 + w3)), so the result
 // stays deterministic.  Only the codebooks live in LDS during the main loop,
 // which has no barrier.
+//
+// With kQuad, for m <= 8, the same steps feed v_mfma_f32_4x4x1_16b_f32
+// instead: 16 independent 4 x 4 blocks of k = 1, block b = l / 4 made of
+// lanes 4b .. 4b + 3.  The weight operand keeps its place (lane l's value q
+// is column j = l % 4 of its block), and the src1 operand of lane l is src1
+// column 4 bi + l % 4 of the lane's own weight row, so block b sums products
+// of one weight row only.  The tile's 4 kBI dst rows are kBI sets of 4 (set
+// bi's row v is dst row 4 bi + v, accumulator register v), and the lanes of
+// the four weight rows of a step hold partial sums of the same dst elements;
+// they are added across lanes at the end, (g0 + g1) + (g2 + g3) over the lane
+// groups l / 16.  The instruction does a quarter of the 16 x 16 x 4 one's
+// products in about half its time (per call on the output head: 0.19 ms at
+// m <= 4 and 0.25 ms at m <= 8 against 0.28 ms for the 16-row tile, and
+// 0.33 ms with three sets, so m <= 12 keeps the 16-row tile).
 constexpr int kDirectK = 4;   // weight rows per step (n_steps uses >> 2)
 
 template <int kBI>
@@ -684,16 +698,33 @@ struct DirectLoad {
     float b[kBI];
 };
 
-template <int kBI>
+template <int kBI, bool kQuad>
 struct Direct {
-    static constexpr int kRows = 16 * kBI;          // dst rows of the tile
-    static constexpr int kMinWaves = kBI >= 3 ? 2 : 1;
+    static constexpr int kRows = (kQuad ? 4 : 16) * kBI;  // dst rows of the tile
+    static constexpr int kMinWaves = kBI >= 3 && !kQuad ? 2 : 1;
+
+    // the tile row of the lane's src1 operand of block (or set) bi
+    static __device__ __forceinline__ uint32_t src1_row(int lane, int bi)
+    {
+        return kQuad ? static_cast<uint32_t>(4 * bi + (lane & 3))
+                     : static_cast<uint32_t>(kBI * (lane & 15) + bi);
+    }
+
+    static __device__ __forceinline__ f32x4 mma(float b, float w, f32x4 acc)
+    {
+        if constexpr (kQuad)
+            return __builtin_amdgcn_mfma_f32_4x4x1f32(b, w, acc, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x4f32(b, w, acc, 0, 0, 0);
+    }
 };
 
-template <int kBI, bool kSrc1Transposed>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Direct<kBI>::kMinWaves)))
+template <int kBI, bool kQuad, bool kSrc1Transposed>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Direct<kBI, kQuad>::kMinWaves)))
 void out_prod_direct_kernel(FusedArgs a)
 {
+    using D = Direct<kBI, kQuad>;
     __shared__ float lds_scb[256];
     __shared__ f32x2 lds_pair[256];                  // (entry of low nibble, high nibble)
     __shared__ float lds_red[kBI * 32 * 64];         // a wave's partial tile
@@ -706,7 +737,7 @@ void out_prod_direct_kernel(FusedArgs a)
     const uint32_t rest = blockIdx.x / static_cast<uint32_t>(a.tiles_i);
     const int tj = static_cast<int>(rest % static_cast<uint32_t>(a.tiles_j));
     const int split = static_cast<int>(rest / static_cast<uint32_t>(a.tiles_j));
-    const int64_t i0 = int64_t{ti} * Direct<kBI>::kRows, j0 = int64_t{tj} * kTileJ;
+    const int64_t i0 = int64_t{ti} * D::kRows, j0 = int64_t{tj} * kTileJ;
     const int64_t k_begin = int64_t{split} * a.rows_per_split;
     const int64_t k_end = min(a.n_rows, k_begin + a.rows_per_split);
 
@@ -723,11 +754,11 @@ void out_prod_direct_kernel(FusedArgs a)
     const uint32_t ld_src1 = static_cast<uint32_t>(a.ld);
     const uint32_t col_in = j0 + 8 * c < a.n_cols ? 8u * c : 0u;
     const uint32_t w_elem = static_cast<uint32_t>(row) * n_cols + col_in;
-    const uint32_t i_last = static_cast<uint32_t>(min(a.m - i0, int64_t{Direct<kBI>::kRows}) - 1);
+    const uint32_t i_last = static_cast<uint32_t>(min(a.m - i0, int64_t{D::kRows}) - 1);
     uint32_t b_off[kBI];  // bytes from the step's first src1 element
 #pragma unroll
     for (int bi = 0; bi < kBI; ++bi) {
-        const uint32_t il = min(static_cast<uint32_t>(kBI * c + bi), i_last);
+        const uint32_t il = min(D::src1_row(lane, bi), i_last);
         b_off[bi] = kSrc1Transposed ? 4u * (il * ld_src1 + row) : 4u * (row * ld_src1 + il);
     }
     const int lb = a.log2_block;
@@ -759,9 +790,9 @@ void out_prod_direct_kernel(FusedArgs a)
         const __amdgpu_buffer_rsrc_t b =
             kSrc1Transposed
                 ? span_buffer(a.src1 + (i0 * a.ld + k0),
-                              4u * (Direct<kBI>::kRows * ld_src1 + kDirectK))
+                              4u * (D::kRows * ld_src1 + kDirectK))
                 : span_buffer(a.src1 + (k0 * a.ld + i0),
-                              4u * (kDirectK * ld_src1 + Direct<kBI>::kRows));
+                              4u * (kDirectK * ld_src1 + D::kRows));
 #pragma unroll
         for (int bi = 0; bi < kBI; ++bi)
             ld.b[bi] = load_f32(b, b_off[bi]);
@@ -786,7 +817,7 @@ void out_prod_direct_kernel(FusedArgs a)
 #pragma unroll
             for (int bi = 0; bi < kBI; ++bi)
                 acc[bi][bj] =
-                    __builtin_amdgcn_mfma_f32_16x16x4f32(ld.b[bi], v[bj], acc[bi][bj], 0, 0, 0);
+                    D::mma(ld.b[bi], v[bj], acc[bi][bj]);
     };
     // a loaded step that may lie past n_full: its operands zeroed there, so
     // that the accumulators are updated unconditionally (see below)
@@ -797,8 +828,7 @@ void out_prod_direct_kernel(FusedArgs a)
         for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
             for (int bi = 0; bi < kBI; ++bi)
-                acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    use ? ld.b[bi] : 0.0f, use ? v[bj] : 0.0f, acc[bi][bj], 0, 0, 0);
+                acc[bi][bj] = D::mma(use ? ld.b[bi] : 0.0f, use ? v[bj] : 0.0f, acc[bi][bj]);
     };
 
     // Full steps: wave w takes steps w, w + 4, w + 8, ... below n_full.  Two
@@ -869,7 +899,7 @@ void out_prod_direct_kernel(FusedArgs a)
             ld.absmax = a.nested_absmax[(e >> lb) >> kNestedLog2];
 #pragma unroll
             for (int bi = 0; bi < kBI; ++bi) {
-                const int64_t i = i0 + min(static_cast<uint32_t>(kBI * c + bi), i_last);
+                const int64_t i = i0 + min(D::src1_row(lane, bi), i_last);
                 ld.b[bi] = kSrc1Transposed ? a.src1[i * a.ld + r] : a.src1[r * a.ld + i];
             }
         }
@@ -879,8 +909,7 @@ void out_prod_direct_kernel(FusedArgs a)
         for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
             for (int bi = 0; bi < kBI; ++bi)
-                acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    valid ? ld.b[bi] : 0.0f, valid ? v[bj] : 0.0f, acc[bi][bj], 0, 0, 0);
+                acc[bi][bj] = D::mma(valid ? ld.b[bi] : 0.0f, valid ? v[bj] : 0.0f, acc[bi][bj]);
     }
 
     // partial tiles: (w0 + w2) + (w1 + w3), through one LDS buffer in three
@@ -919,22 +948,53 @@ void out_prod_direct_kernel(FusedArgs a)
     if (wave == 1)
         put();
     __syncthreads();
-    if (wave != 0 || j0 + 8 * c >= a.n_cols)
+    if (wave != 0)
         return;
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
+    if constexpr (kQuad) {
+        // the lane groups of the four weight rows, (g0 + g1) + (g2 + g3), with
+        // every lane of the wave still active for the exchanges
 #pragma unroll
-    for (int bi = 0; bi < kBI; ++bi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            // the accumulator's row 4 * row + v (see Shape::acc_row) of block bi
-            const int64_t i = i0 + kBI * (4 * row + v) + bi;
-            if (i >= a.m)
-                continue;
-            float *o = out + i * a.n_cols + j0 + 8 * c;
+        for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
-                o[bj] = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
-        }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float x = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
+                    x = x + __shfl_xor(x, 16);
+                    acc[bi][bj][v] = x + __shfl_xor(x, 32);
+                }
+        if (row != 0 || j0 + 8 * c >= a.n_cols)
+            return;
+#pragma unroll
+        for (int bi = 0; bi < kBI; ++bi)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t i = i0 + 4 * bi + v;  // the accumulator's row v of set bi
+                if (i >= a.m)
+                    continue;
+                float *o = out + i * a.n_cols + j0 + 8 * c;
+#pragma unroll
+                for (int bj = 0; bj < 8; ++bj)
+                    o[bj] = acc[bi][bj][v];
+            }
+    } else {
+        if (j0 + 8 * c >= a.n_cols)
+            return;
+#pragma unroll
+        for (int bi = 0; bi < kBI; ++bi)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // the accumulator's row 4 * row + v (see Shape::acc_row) of block bi
+                const int64_t i = i0 + kBI * (4 * row + v) + bi;
+                if (i >= a.m)
+                    continue;
+                float *o = out + i * a.n_cols + j0 + 8 * c;
+#pragma unroll
+                for (int bj = 0; bj < 8; ++bj)
+                    o[bj] = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
+            }
+    }
 }
 
 // dst[x] = part[0][x] + part[1][x] + ... in split order.  Each thread loads
@@ -982,7 +1042,7 @@ int64_t ceil_div(int64_t a, int64_t b)
 // The kernel for a launch: on the aligned path the direct kernel for m <= 64
 // (16, 32, 48 or 64 rows per tile); 16-row tiles for decode-sized m on the
 // byte path; else the width of least tile_cost.
-// `variant` (0..23) indexes the kernel for the occupancy cache.
+// `variant` (0..27) indexes the kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
     int tile_i;
@@ -1013,11 +1073,12 @@ double tile_cost(int64_t m, int64_t tile_i)
     return static_cast<double>(ceil_div(m, tile_i) * tile_i) * rel;
 }
 
-template <int kBI>
+template <int kBI, bool kQuad = false>
 const void *direct_kernel(bool transposed)
 {
-    return transposed ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, true>)
-                      : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, false>);
+    return transposed
+               ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kQuad, true>)
+               : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kQuad, false>);
 }
 
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
@@ -1025,6 +1086,10 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
     const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
     if (m <= 64 && aligned8) {
         const int t = transposed ? 1 : 0;
+        if (m <= 4)
+            return {direct_kernel<1, true>(transposed), 4, 24 + t};
+        if (m <= 8)
+            return {direct_kernel<2, true>(transposed), 8, 26 + t};
         if (m <= 16)
             return {direct_kernel<1>(transposed), 16, 16 + t};
         if (m <= 32)
@@ -1049,7 +1114,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
             4 + sub};
 }
 
-constexpr int kVariants = 24;
+constexpr int kVariants = 28;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

@@ -43,7 +43,7 @@ def test_kernels_present(asm):
                           ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
                           ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
-                          ("out_prod_fused_kernel", 14), ("out_prod_direct_kernel", 8),
+                          ("out_prod_fused_kernel", 14), ("out_prod_direct_kernel", 12),
                           ("out_prod_reduce_kernel", 1),
                           ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1),
                           ("dq4_shift_tile_kernel", 23)):
@@ -62,9 +62,12 @@ def test_no_fused_or_packed_fp_instructions(asm):
                 or "out_prod_direct" in name):
             assert "v_add_f32" in code, name   # the scale is rebuilt in the fused kernels
         if "out_prod_fused" in name or "out_prod_direct" in name:  # FP32 matrix cores only
-            want = ({"v_mfma_f32_16x16x4_f32"}
-                    if "kernelILi16E" in name or "out_prod_direct" in name
-                    else {"v_mfma_f32_32x32x2_f32"})
+            if re.search(r"out_prod_direct_kernelILi\dELb1E", name):  # the 4-row sets
+                want = {"v_mfma_f32_4x4x1_16b_f32"}
+            elif "kernelILi16E" in name or "out_prod_direct" in name:
+                want = {"v_mfma_f32_16x16x4_f32"}
+            else:
+                want = {"v_mfma_f32_32x32x2_f32"}
             assert set(re.findall(r"\bv_mfma\w*", code)) == want, name
 
 

@@ -152,20 +152,21 @@ def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
 def test_direct_tiles_steps_and_splits(n_rows, transposed):
-    """m <= 64 on the aligned path takes the direct kernel (16, 32, 48 or 64
-    dst rows per tile, the rows permuted within the tile): 4-row steps spread
-    over the workgroup's 4 waves, its full steps pipelined, the split's last
-    partial step checked, and the waves' partial tiles added at the end.  Row
-    counts below, at and just past a step and a wave round, a ragged last
-    128-column tile, and m at and past each tile width and ragged within it
-    (with and without row splits): dst row i equals the oracle's weight row
-    sel[i]."""
+    """m <= 64 on the aligned path takes the direct kernel (4 or 8 dst rows
+    per tile on the 4 x 4 x 1 matrix instruction, whose lane groups are added
+    at the end; 16, 32, 48 or 64 rows on the 16 x 16 x 4 one, permuted within
+    the tile): 4-row steps spread over the workgroup's 4 waves, its
+    full steps pipelined, the split's last partial step checked, and the
+    waves' partial tiles added at the end.  Row counts below, at and just
+    past a step and a wave round, a ragged last 128-column tile, and m at and
+    past each tile width and ragged within it (with and without row splits):
+    dst row i equals the oracle's weight row sel[i]."""
     n_cols = 136
     x = inputs.make_inputs(n_rows * n_cols, 32, "fp4", 0.07, seed=n_rows + 901,
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
-    for m in (1, 7, 16, 17, 32, 33, 45, 48, 49, 64):
+    for m in (1, 3, 4, 5, 7, 8, 9, 12, 13, 16, 17, 32, 33, 45, 48, 49, 64):
         rng = np.random.Generator(np.random.PCG64(n_rows * 17 + m))
         sel = rng.integers(0, n_rows, size=m)
         b = np.zeros((n_rows, m), np.float32)
@@ -206,7 +207,7 @@ def test_staged_tile_keeps_checked_loads_past_32_bit_offsets():
 
 
 @pytest.mark.parametrize("transposed", [False, True])
-@pytest.mark.parametrize("m", [16, 48, 100])
+@pytest.mark.parametrize("m", [3, 12, 16, 48, 100])
 def test_infinite_src1_reaches_only_its_own_products(m, transposed):
     """An infinity in src1 must reach exactly the dst elements the sum gives
     it: each workgroup reads only the rows of its own split, and zeroes both
@@ -214,8 +215,8 @@ def test_infinite_src1_reaches_only_its_own_products(m, transposed):
     elsewhere.  One +inf per src1 column at a random row (the rows cover many
     splits); the NaN and infinity pattern of dst, and the infinities' signs,
     equal those of inf * W[r][j] added to the finite part, and every other
-    element is finite (direct tiles at m = 16 and 48, the staged tile at
-    m = 100)."""
+    element is finite (direct tiles at m = 3, 12, 16 and 48, the staged tile
+    at m = 100)."""
     n_rows, n_cols = 4099, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=780 + m, n_rows=n_rows,
                            n_cols=n_cols)
@@ -281,12 +282,12 @@ def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
                                           f"workspace={'preferred' if ws is None else 'none'}")
 
 
-@pytest.mark.parametrize("m", [16, 32, 48, 64, 512])
+@pytest.mark.parametrize("m", [4, 8, 16, 32, 48, 64, 512])
 def test_selection_output_head_is_bit_exact(m):
     """Selection-matrix src1 over the 151 936 x 5 376 output head, both
-    orientations, at each tile of the direct kernel (16, 32, 48 and 64 rows)
-    and the staged 256-row tile: every row split is selected; dst equals the
-    weight rows exactly."""
+    orientations, at each tile of the direct kernel (4, 8, 16, 32, 48 and 64
+    rows) and the staged 256-row tile: every row split is selected; dst
+    equals the weight rows exactly."""
     wl = inputs.OUTPUT_HEAD
     x = cases.output_head_weight()
     dev = dq4.to_device(x)
