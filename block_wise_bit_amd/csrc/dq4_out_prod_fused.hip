@@ -102,7 +102,7 @@ struct FusedArgs {
     int log2_block;
     int tiles_i;
     int tiles_j;
-    int full_stages;         // 1: full stages take the unchecked loads (offsets fit 32 bits)
+    int full_stages;         // 1: full stages (steps) take the unchecked loads (offsets fit 32 bits)
 };
 
 // Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
@@ -769,33 +769,46 @@ void out_prod_direct_kernel(FusedArgs a)
     const int n_full =
         a.full_stages ? __builtin_amdgcn_readfirstlane(static_cast<int>(rows >> 2)) : 0;
 
-    // a full step: uniform bases plus the lane constants, no bounds checks
+    // A full step: no bounds checks, one buffer per array for the whole split
+    // and 32-bit offsets, the step's part of them uniform (the instruction's
+    // scalar offset, or added once for the lanes' shared block index).  The
+    // host allows full steps only when the split's offsets below stay under
+    // 2^32: rows * n_cols weight elements plus the block offset bl0 < 4096,
+    // and rows * ld (or kRows * ld when transposed) src1 floats.  Rebuilding
+    // the buffers at every step instead cost about 40 scalar instructions a
+    // step, up to 18 % of the call at m <= 8.
+    const int64_t e_split = k_begin * a.n_cols + j0;  // the split's first element of the tile
+    const int64_t bh0 = e_split >> lb;
+    const uint32_t rows32 = static_cast<uint32_t>(rows);
+    const uint32_t span_e = rows32 * n_cols;  // elements from e_split to the split's end
+    const __amdgpu_buffer_rsrc_t packed_b =
+        span_buffer(a.packed + (e_split >> 1), span_e / 2 + 64);
+    const uint32_t bl0 = static_cast<uint32_t>(e_split & ((int64_t{1} << lb) - 1));
+    const uint32_t c_span = ((bl0 + span_e + 128u) >> lb) + 1u;
+    const __amdgpu_buffer_rsrc_t code_b = span_buffer(a.scale_codes + bh0, c_span);
+    const uint32_t g0 = static_cast<uint32_t>(bh0 & ((1 << kNestedLog2) - 1));
+    const __amdgpu_buffer_rsrc_t absmax_b =
+        span_buffer(a.nested_absmax + (bh0 >> kNestedLog2),
+                    4u * (((g0 + c_span) >> kNestedLog2) + 1u));
+    const __amdgpu_buffer_rsrc_t src1_b =
+        kSrc1Transposed
+            ? span_buffer(a.src1 + (i0 * a.ld + k_begin), 4u * (D::kRows * ld_src1 + rows32))
+            : span_buffer(a.src1 + (k_begin * a.ld + i0), 4u * (rows32 * ld_src1 + D::kRows));
+    const uint32_t w_byte = w_elem >> 1, c_lane = bl0 + w_elem;
+    const uint32_t step_elems = kDirectK * n_cols;
+    const uint32_t step_b = kSrc1Transposed ? 4u * kDirectK : 4u * kDirectK * ld_src1;
     const auto load_full = [&](int s) {
         DirectLoad<kBI> ld;
-        const int64_t k0 = k_begin + int64_t{kDirectK} * s;
-        const int64_t e0 = k0 * a.n_cols + j0;  // a multiple of 8
-        ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(
-            span_buffer(a.packed + (e0 >> 1), kDirectK / 2 * n_cols), w_elem >> 1, 0, 0);
-        const int64_t bh = e0 >> lb;
-        const uint32_t bl = static_cast<uint32_t>(e0 & ((int64_t{1} << lb) - 1));
-        const uint32_t cb = (bl + w_elem) >> lb;
-        const uint32_t c_span = ((kDirectK * n_cols + 4095u) >> lb) + 1u;
-        ld.code = __builtin_amdgcn_raw_buffer_load_b8(span_buffer(a.scale_codes + bh, c_span),
-                                                      cb, 0, 0);
-        const uint32_t g =
-            (static_cast<uint32_t>(bh & ((1 << kNestedLog2) - 1)) + cb) >> kNestedLog2;
-        ld.absmax = load_f32(span_buffer(a.nested_absmax + (bh >> kNestedLog2),
-                                         4u * ((c_span + 255u) / 256u + 1u)),
-                             4u * g);
-        const __amdgpu_buffer_rsrc_t b =
-            kSrc1Transposed
-                ? span_buffer(a.src1 + (i0 * a.ld + k0),
-                              4u * (D::kRows * ld_src1 + kDirectK))
-                : span_buffer(a.src1 + (k0 * a.ld + i0),
-                              4u * (kDirectK * ld_src1 + D::kRows));
+        const uint32_t d = static_cast<uint32_t>(s) * step_elems;  // the step's first element
+        ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(packed_b, w_byte, d >> 1, 0);
+        const uint32_t cb = (c_lane + d) >> lb;  // the lane's block, from bh0
+        ld.code = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb, 0, 0);
+        ld.absmax = load_f32(absmax_b, 4u * ((g0 + cb) >> kNestedLog2));
+        const uint32_t sb = static_cast<uint32_t>(s) * step_b;
 #pragma unroll
         for (int bi = 0; bi < kBI; ++bi)
-            ld.b[bi] = load_f32(b, b_off[bi]);
+            ld.b[bi] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(src1_b, b_off[bi], sb, 0));
         return ld;
     };
 
@@ -845,13 +858,20 @@ void out_prod_direct_kernel(FusedArgs a)
     constexpr int kBank = 4 * kDepth;  // steps of one bank
     DirectLoad<kBI> bank0[kDepth], bank1[kDepth];
     if (n_full > 0) {
-        // unconditional as in the loop (past n_full: step n_full - 1, unused)
+        // unconditional as in the loop (past n_full: step n_full - 1, unused),
+        // and issued in the loop's order: the counts of loads in flight that
+        // the loop waits for hold on entry too (left to reorder these loads,
+        // the compiler made the loop wait for all but a few of them)
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d)
+        for (int d = 0; d < kDepth; ++d) {
             bank0[d] = load_full(min(wave + 4 * d, n_full - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d)
+        for (int d = 0; d < kDepth; ++d) {
             bank1[d] = load_full(min(wave + kBank + 4 * d, n_full - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     int s0 = wave;  // first step of bank0
     for (; s0 + kBank + 4 * (kDepth - 1) < n_full; s0 += 2 * kBank) {
@@ -1047,6 +1067,7 @@ struct Plan {
     const void *kernel;
     int tile_i;
     int variant;
+    bool direct;  // out_prod_direct_kernel (full steps), else the staged kernel (full stages)
 };
 
 template <int kTileI, bool kSrc1Transposed>
@@ -1087,31 +1108,31 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
     if (m <= 64 && aligned8) {
         const int t = transposed ? 1 : 0;
         if (m <= 4)
-            return {direct_kernel<1, true>(transposed), 4, 24 + t};
+            return {direct_kernel<1, true>(transposed), 4, 24 + t, true};
         if (m <= 8)
-            return {direct_kernel<2, true>(transposed), 8, 26 + t};
+            return {direct_kernel<2, true>(transposed), 8, 26 + t, true};
         if (m <= 16)
-            return {direct_kernel<1>(transposed), 16, 16 + t};
+            return {direct_kernel<1>(transposed), 16, 16 + t, true};
         if (m <= 32)
-            return {direct_kernel<2>(transposed), 32, 18 + t};
+            return {direct_kernel<2>(transposed), 32, 18 + t, true};
         if (m <= 48)
-            return {direct_kernel<3>(transposed), 48, 22 + t};
-        return {direct_kernel<4>(transposed), 64, 20 + t};
+            return {direct_kernel<3>(transposed), 48, 22 + t, true};
+        return {direct_kernel<4>(transposed), 64, 20 + t, true};
     }
     if (m <= 16)
-        return {transposed ? kernel_for<16, true>(false) : kernel_for<16, false>(false), 16, sub};
+        return {transposed ? kernel_for<16, true>(false) : kernel_for<16, false>(false), 16, sub, false};
     int64_t best = 64;
     for (const int64_t w : {128, 256})
         if (tile_cost(m, w) < tile_cost(m, best))
             best = w;
     if (best == 256)
         return {transposed ? kernel_for<256, true>(aligned8) : kernel_for<256, false>(aligned8),
-                256, 12 + sub};
+                256, 12 + sub, false};
     if (best == 128)
         return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
-                128, 8 + sub};
+                128, 8 + sub, false};
     return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64,
-            4 + sub};
+            4 + sub, false};
 }
 
 constexpr int kVariants = 28;
@@ -1178,6 +1199,21 @@ bool full_stages_fit(int64_t n_cols, int64_t ld, int tile_i, bool transposed)
     if (ld >= k32 / 4 / rows)
         return false;
     return 4 * (rows * ld + tile_i + kStage) < k32;
+}
+
+// Whether the direct kernel's full steps may address a split of `rows` rows
+// (at most) from one base per array with 32-bit offsets: its rows * n_cols
+// weight elements plus a block offset under 4096 (and the lanes' columns),
+// and the floats of src1 it reads -- rows * ld + tile_i, or tile_i * ld +
+// rows when transposed -- as bytes.  Otherwise every step takes the checked
+// loads.
+bool direct_split_fits(int64_t rows, int64_t n_cols, int64_t ld, int tile_i, bool transposed)
+{
+    constexpr int64_t k32 = int64_t{1} << 32, kFloats = k32 / 4;
+    if (rows >= k32 / n_cols || rows * n_cols + 8192 >= k32)
+        return false;
+    return transposed ? ld < kFloats / tile_i && tile_i * ld + rows < kFloats
+                      : ld < kFloats / rows && rows * ld + tile_i < kFloats;
 }
 
 dq4_status_t grid_size(int64_t count, int device, uint32_t *grid)
@@ -1273,8 +1309,11 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kStage) > 0x7FFFFFFF)
         return DQ4_EUNSUPPORTED;  // the kernel counts a split's stages in 32 bits
 
-    const bool full = aligned8 && dq4::full_stages_fit(n_cols, ld_src1, plan.tile_i,
-                                                       src1_transposed != 0);
+    const bool full =
+        aligned8 && (plan.direct ? dq4::direct_split_fits(rps, n_cols, ld_src1, plan.tile_i,
+                                                         src1_transposed != 0)
+                                 : dq4::full_stages_fit(n_cols, ld_src1, plan.tile_i,
+                                                        src1_transposed != 0));
     dq4::FusedArgs a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, src1,
                      splits > 1 ? workspace : dst, n_rows, n_cols, m, ld_src1, rps, offset,
                      log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j),

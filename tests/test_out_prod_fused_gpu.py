@@ -124,12 +124,12 @@ def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
 
 
 def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
-    """A transposed src1 whose leading dimension puts its 16 columns of a
-    tile more than 2^32 bytes apart: the unchecked stages' 32-bit lane
-    offsets would not fit, so every stage takes the checked loads; the bits
+    """A transposed src1 whose leading dimension puts the 4 columns of the
+    m = 2 tile more than 2^32 bytes apart: the unchecked steps' 32-bit
+    offsets would not fit, so every step takes the checked loads; the bits
     equal those of the same call on a compact src1 and the oracle's rows."""
     n_rows, n_cols, m = 16 * 9 + 3, 256, 2
-    ld = (1 << 26) + 64
+    ld = (1 << 28) + 64
     x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", -0.03, seed=778, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
@@ -147,6 +147,33 @@ def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
     assert np.array_equal(y_wide.view(np.uint32), y_compact.view(np.uint32))
     assert np.array_equal(y_wide, w[sel])
     del flat, wide
+
+
+def test_split_past_2_pow_32_weight_elements_keeps_the_checked_loads():
+    """A weight of 2^32 + 2^20 elements (2 GiB packed) in one split, with no
+    workspace: the split's weight offsets pass 2^32, so every step of the
+    direct tile takes the checked 64-bit loads; with the preferred workspace
+    the splits are small enough for the unchecked ones.  Selected rows at
+    the start, on both sides of element 2^32 and at the end equal the
+    oracle's rows in both calls."""
+    n_rows, n_cols = (1 << 20) + 256, 4096
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=782, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    sel = np.array([0, (1 << 20) - 1, 1 << 20, n_rows - 1])  # element 2^32 starts row 2^20
+    m = len(sel)
+    b = np.zeros((n_rows, m), np.float32)
+    b[sel, np.arange(m)] = 1.0
+    want = weight_rows(x, n_cols, sel)
+    for ws in (torch.empty(0, device="cuda"), None):
+        y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows, n_cols=n_cols,
+                                   blocksize=64, src1=_src1(b, False), src1_transposed=False,
+                                   workspace=ws).cpu().numpy()
+        bad = np.argwhere(y != want)
+        assert bad.size == 0, (f"workspace={'none' if ws is not None else 'preferred'}: "
+                               f"first mismatch at (i, j) = {tuple(bad[0])}")
+    del dev
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("transposed", [False, True])
