@@ -328,10 +328,13 @@ def test_selection_output_head_is_bit_exact(m):
                               f"fused output head m={m} transposed={transposed}")
 
 
-def test_output_head_both_orientations_and_against_the_blocked_route():
-    """The 151936 x 5376 output head at m = 16 in both orientations; the fused
-    and the row-blocked results agree within twice the summation bound."""
-    case = cases.OUTPUT_HEAD
+@pytest.mark.parametrize("m", [4, 16])
+def test_output_head_both_orientations_and_against_the_blocked_route(m):
+    """The 151936 x 5376 output head with random src1 at m = 4 (the 4-row
+    set, whose lane groups add up at the end) and m = 16, both orientations,
+    within the summation bound; the fused and the row-blocked results agree
+    within twice the bound."""
+    case = dict(cases.OUTPUT_HEAD, m=m)
     n_rows, n_cols = case["n_rows"], case["n_cols"]
     x = cases.output_head_weight()
     dev = dq4.to_device(x)
@@ -402,12 +405,14 @@ def test_edge_cases():
                                                                 device="cuda"))
 
 
-def test_graph_capture_replays_with_splits():
+@pytest.mark.parametrize("m", [4, 32])
+def test_graph_capture_replays_with_splits(m):
     """The fused route -- kernel plus the reduction over row splits -- captured
     in a HIP graph and replayed several times, with new src1 values written
     eagerly between replays: every replay equals an eager call on the same
-    src1 bit for bit (the result is deterministic for a given workspace)."""
-    n_rows, n_cols, m = 20000, 384, 32
+    src1 bit for bit (the result is deterministic for a given workspace).
+    m = 4 takes the 4-row set, m = 32 the 32-row tile."""
+    n_rows, n_cols = 20000, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=20000, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
