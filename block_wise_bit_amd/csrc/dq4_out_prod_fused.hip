@@ -8,47 +8,36 @@
 //
 //   dst[i][j] = sum_r B[r][i] * W[r][j]     dst: m x n_cols FP32, row-major
 //
-// but each workgroup decodes the 4-bit weight of its tile straight into LDS
-// as the very FP32 values the dequantization kernel writes (bitsandbytes
-// issue "Fuse nested scale reconstruction into SM103 4-bit dequantization",
+// but each workgroup decodes the 4-bit weight of its tile on chip as the
+// very FP32 values the dequantization kernel writes (bitsandbytes issue
+// "Fuse nested scale reconstruction into SM103 4-bit dequantization",
 // section "Proposed experiment": W = fl32(codebook4[k] * scale) with scale =
-// fl32(fl32(scale_codebook[code] * absmax) + offset)), and feeds them to
-// v_mfma_f32_32x32x2_f32.
+// fl32(fl32(scale_codebook[code] * absmax) + offset)) and feeds them to the
+// FP32 matrix instructions.
 //
 // Design:
-//  * a workgroup (4 waves) owns a kTileI x 128 tile of dst (kTileI values of
-//    i, the src1 columns: 256, 128 or 64, or 16 for decode-sized m; 128 of
-//    j, the weight columns) and one split of the rows r; its waves form a
-//    2 x 2 grid, each computing 32 x 32 MFMA blocks that share their
-//    operands along i and j.  The decode of a stage costs the same at every
-//    kTileI while the MFMAs grow with it, and on gfx950 vector instructions
-//    barely overlap FP32 MFMAs, so wider tiles cost less per row (256 rows:
-//    ~5 % over 128 at m >= 512; its 188 registers, 128 of them accumulators,
-//    leave two waves per SIMD); a ragged m pays for the padded rows of its
-//    last tile, so the width comes from a cost rule (tile_cost);
-//  * per stage of 16 weight rows every lane decodes 8 consecutive weight
-//    elements (one packed dword when n_cols % 8 == 0, and then one block
-//    scale, since the 8 elements share a block; else one or two scales),
-//    looking both entries of each packed byte up at once in a table of
-//    codebook pairs (except in the 256-row tile), and stages the tile's src1
-//    values;
-//  * two LDS buffers: the waves decode the next stage into one while the
-//    MFMAs read the other, and the global loads of the stage after that are
-//    issued before the barrier, so each stage costs one barrier and its
-//    loads fly during the next stage's MFMAs; the stage loop is unrolled by
-//    two, so every LDS address is a lane-constant register plus an
-//    immediate;
-//  * every stage but a split's last holds kStage rows of the split: on the
-//    aligned path its loads are a uniform base plus a lane-constant 32-bit
-//    offset, with no bounds checks (lanes past n_cols or m read in-range
-//    bytes whose products land only in dst elements that are never stored),
-//    which halves the vector instructions of a stage (9 % faster at m = 64,
-//    2-11 % at the other widths); the last stage keeps the checked loads;
-//  * small m (at most 64) on the aligned path takes a direct kernel that
-//    decodes each packed dword straight into the matrix instruction's
-//    operand registers, with no LDS staging of the weights and no barrier in
-//    its main loop (out_prod_direct_kernel: 1.4 x the staged kernel at
-//    m = 16, 2 x at m = 32, 1.3 x at m = 48, level at m = 64);
+//  * the aligned path (n_cols % 8 == 0, packed 4-byte aligned) takes the
+//    direct kernel (out_prod_direct_kernel): each lane decodes a packed
+//    dword of 8 weights, which share one block scale, straight into the
+//    operand registers of the matrix instruction, with no LDS staging of the
+//    weights and no barrier in its main loop.  A tile is 4 or 8 dst rows
+//    (v_mfma_f32_4x4x1_16b_f32) or 16, 32, 48 or 64 rows
+//    (v_mfma_f32_16x16x4_f32) by 128 columns; m > 64 is split into whole
+//    64-row tiles and one launch for the rest with the smallest tile that
+//    holds it (row_ranges), since the 64-row tile costs no more per dst row
+//    than any wider staged tile.  Full steps address the split from one
+//    buffer per array with 32-bit offsets when those fit, and the split's
+//    last step, or every step when they do not, takes checked 64-bit loads;
+//  * the byte path (odd widths) takes the staged kernel
+//    (out_prod_fused_kernel): a workgroup (4 waves) owns a kTileI x 128 tile
+//    of dst (kTileI = 256, 128 or 64 from a cost rule, tile_cost, or 16 for
+//    decode-sized m) and one split of the rows; per stage of 16 weight rows
+//    every lane decodes 8 consecutive elements byte by byte (one or two
+//    block scales) into LDS and stages the tile's src1 values, and the
+//    waves' 32 x 32 (or 16 x 16) MFMA blocks read both from LDS; two LDS
+//    buffers, so the next stage is decoded while the MFMAs read the current
+//    one, with one barrier per stage and the stage after that already
+//    loading;
 //  * the rows are split when that fills the GPU's resident workgroup slots
 //    (sized from the kernel's occupancy) better than the tiles alone; each
 //    split writes its partial tile to the caller's workspace, and a second
@@ -102,7 +91,7 @@ struct FusedArgs {
     int log2_block;
     int tiles_i;
     int tiles_j;
-    int full_stages;         // 1: full stages (steps) take the unchecked loads (offsets fit 32 bits)
+    int full_stages;         // 1: the direct kernel's full steps take the unchecked loads
 };
 
 // Tile shape: a workgroup owns kTileI x kTileJ of dst and its 4 waves split
@@ -110,7 +99,8 @@ struct FusedArgs {
 // 256: 2 x 2 waves of 32 x 32 blocks (v_mfma_f32_32x32x2_f32, 2 rows per
 // instruction).  kTileI = 16, for decode-sized m on the byte path: 1 x 4
 // waves of 16 x 16 blocks (v_mfma_f32_16x16x4_f32, 4 rows per instruction);
-// on the aligned path m <= 64 takes out_prod_direct_kernel instead.
+// the staged kernel serves the byte path (n_cols % 8 != 0, or packed not
+// 4-byte aligned); the aligned path takes out_prod_direct_kernel.
 template <int kTileI>
 struct Shape {
     static constexpr bool kSmall = kTileI == 16;
@@ -132,13 +122,6 @@ struct Shape {
     // together at the end) remove both (~3 % at m <= 16).  The wider tiles
     // already interleave enough blocks.
     static constexpr int kSets = kSmall ? 2 : 1;
-    // The aligned decode reads both entries of a packed byte at once from a
-    // 256-entry table of codebook pairs (one 8-byte LDS read and one byte
-    // select per two elements: 11 fewer vector and 4 fewer LDS instructions
-    // per stage; 1-3 % faster at m = 128).  The 256-row tile leaves it out:
-    // its 2 KiB of LDS would cost that tile a resident workgroup per CU (2 %
-    // slower at m = 512); the 16-row tile only runs the byte path.
-    static constexpr bool kPairTable = kTileI == 64 || kTileI == 128;
     // Waves per SIMD the register allocation must allow: the wide tiles'
     // LDS already caps them at 2 (256 rows) and 4 (128 rows) per SIMD, and
     // left alone the compiler spends registers on hoisted LDS addresses until
@@ -167,8 +150,7 @@ struct Shape {
 // What one lane loads from HBM for one stage, before decoding it.
 template <int kTileI>
 struct StageLoad {
-    uint32_t packed4;   // 8 nibbles (kAligned8) ...
-    uint8_t bytes[8];   // ... or the byte holding each element (otherwise)
+    uint8_t bytes[8];   // the byte holding each element
     uint32_t code_lo, code_hi;
     float absmax_lo, absmax_hi;
     float b[Shape<kTileI>::kB];
@@ -178,10 +160,9 @@ template <int kTileI, bool kSrc1Transposed>
 __device__ __forceinline__ void load_stage_b(const FusedArgs &a, int64_t k0, int64_t k_end,
                                              int64_t i0, int t, StageLoad<kTileI> &ld);
 
-// kAligned8: n_cols % 8 == 0 and packed 4-byte aligned, so a lane's 8
-// consecutive elements are one aligned packed dword and are all in range
-// together.
-template <int kTileI, bool kSrc1Transposed, bool kAligned8>
+// A lane's 8 consecutive elements, byte by byte: a row's elements need not
+// start on a byte (odd n_cols) and may span two blocks.
+template <int kTileI, bool kSrc1Transposed>
 __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
                                            int64_t i0, int64_t j0, int t,
                                            StageLoad<kTileI> &ld)
@@ -192,24 +173,15 @@ __device__ __forceinline__ void load_stage(const FusedArgs &a, int64_t k0, int64
     const int lb = a.log2_block;
     if (r < k_end && j < a.n_cols) {
         const int64_t e = r * a.n_cols + j;
-        int64_t e_last = e + 7;
-        if constexpr (kAligned8) {
-            ld.packed4 = *reinterpret_cast<const uint32_t *>(a.packed + (e >> 1));
-        } else {
-            e_last = e + (min(a.n_cols - j, int64_t{8}) - 1);
+        const int64_t e_last = e + (min(a.n_cols - j, int64_t{8}) - 1);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                ld.bytes[q] = e + q <= e_last ? a.packed[(e + q) >> 1] : 0;
-        }
+        for (int q = 0; q < 8; ++q)
+            ld.bytes[q] = e + q <= e_last ? a.packed[(e + q) >> 1] : 0;
         const int64_t b_lo = e >> lb, b_hi = e_last >> lb;  // at most two blocks
         ld.code_lo = a.scale_codes[b_lo];
         ld.absmax_lo = a.nested_absmax[b_lo >> kNestedLog2];
-        if constexpr (!kAligned8) {
-            // with kAligned8, e is a multiple of 8 and so is the block size
-            // (a power of two >= 32): the 8 elements share block b_lo
-            ld.code_hi = a.scale_codes[b_hi];
-            ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
-        }
+        ld.code_hi = a.scale_codes[b_hi];
+        ld.absmax_hi = a.nested_absmax[b_hi >> kNestedLog2];
     }
     load_stage_b<kTileI, kSrc1Transposed>(a, k0, k_end, i0, t, ld);
 }
@@ -256,27 +228,18 @@ __device__ __forceinline__ void load_stage_b(const FusedArgs &a, int64_t k0, int
 
 // The 8 weights of one packed dword (element 2p in the low nibble of byte
 // p, element 2p + 1 in its high nibble), all in the block of scale s:
-// v[q] = fl32(codebook4[nibble q] * s).  With the pair table, one 8-byte LDS
-// read returns both entries of a byte.
-template <bool kPairTable>
-__device__ __forceinline__ void decode8(uint32_t packed4, float s, const float *lds_cb4,
-                                        const f32x2 *lds_pair, float (&v)[8])
+// v[q] = fl32(codebook4[nibble q] * s).  One 8-byte LDS read from the
+// 256-entry table of codebook pairs returns both entries of a byte.
+__device__ __forceinline__ void decode8(uint32_t packed4, float s, const f32x2 *lds_pair,
+                                        float (&v)[8])
 {
-    if constexpr (kPairTable) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t off = ((packed4 >> (8 * p)) & 0xFFu) << 3;
-            const f32x2 e = *reinterpret_cast<const f32x2 *>(
-                reinterpret_cast<const char *>(lds_pair) + off);
-            v[2 * p] = e.x * s;
-            v[2 * p + 1] = e.y * s;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t k = (packed4 >> (4 * q)) & 0xFu;
-            v[q] = lds_cb4[k] * s;
-        }
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t off = ((packed4 >> (8 * p)) & 0xFFu) << 3;
+        const f32x2 e =
+            *reinterpret_cast<const f32x2 *>(reinterpret_cast<const char *>(lds_pair) + off);
+        v[2 * p] = e.x * s;
+        v[2 * p + 1] = e.y * s;
     }
 }
 
@@ -301,11 +264,10 @@ __device__ __forceinline__ void store_stage_b(int t, const StageLoad<kTileI> &ld
     }
 }
 
-template <int kTileI, bool kSrc1Transposed, bool kAligned8>
+template <int kTileI, bool kSrc1Transposed>
 __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
                                              int64_t j0, int t, const StageLoad<kTileI> &ld,
                                              const float *lds_scb, const float *lds_cb4,
-                                             const f32x2 *lds_pair,
                                              float (*lds_w)[kLdsW],
                                              float (*lds_b)[Shape<kTileI>::kLdsB])
 {
@@ -315,24 +277,19 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     float v[8];
     if (r < k_end && j < a.n_cols) {
         const float s_lo = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
-        if constexpr (kAligned8) {
-            decode8<Shape<kTileI>::kPairTable>(ld.packed4, s_lo, lds_cb4, lds_pair, v);  // one block (see load_stage)
-        } else {
-            const int lb = a.log2_block;
-            const int64_t e = r * a.n_cols + j;
-            const float s_hi = block_scale(lds_scb[ld.code_hi], ld.absmax_hi, a.offset);
-            // position of element e in its block; element e + q is in the next
-            // block once off + q reaches the block size
-            const uint32_t off = static_cast<uint32_t>(e & ((int64_t{1} << lb) - 1));
-            const int64_t n_valid = min(a.n_cols - j, int64_t{8});
-            const uint32_t odd = static_cast<uint32_t>(e & 1);
+        const int lb = a.log2_block;
+        const int64_t e = r * a.n_cols + j;
+        const float s_hi = block_scale(lds_scb[ld.code_hi], ld.absmax_hi, a.offset);
+        // position of element e in its block; element e + q is in the next
+        // block once off + q reaches the block size
+        const uint32_t off = static_cast<uint32_t>(e & ((int64_t{1} << lb) - 1));
+        const int64_t n_valid = min(a.n_cols - j, int64_t{8});
+        const uint32_t odd = static_cast<uint32_t>(e & 1);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t k =
-                    ((odd + q) & 1) ? (ld.bytes[q] >> 4) : (ld.bytes[q] & 0xFu);
-                const float s = ((off + q) >> lb) == 0 ? s_lo : s_hi;
-                v[q] = q < n_valid ? lds_cb4[k] * s : 0.0f;
-            }
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t k = ((odd + q) & 1) ? (ld.bytes[q] >> 4) : (ld.bytes[q] & 0xFu);
+            const float s = ((off + q) >> lb) == 0 ? s_lo : s_hi;
+            v[q] = q < n_valid ? lds_cb4[k] * s : 0.0f;
         }
     } else {
 #pragma unroll
@@ -345,52 +302,8 @@ __device__ __forceinline__ void decode_stage(const FusedArgs &a, int64_t k0, int
     store_stage_b<kTileI, kSrc1Transposed>(t, ld, lds_b);
 }
 
-// Full stages of the aligned path.  A stage is full when all kStage of its
-// rows are in the split; every stage but a split's last is.  Each address of
-// a full stage is a uniform base (scalar registers, advanced per stage) plus
-// a lane-constant 32-bit offset, so the loads spend no vector instructions
-// on 64-bit index arithmetic and the stage needs no bounds checks: lanes
-// whose weight columns lie past n_cols load column j0's bytes instead, and
-// lanes whose src1 column lies past m (transposed src1) load column i0's;
-// those values only reach dst columns and rows that are never stored (the
-// MFMA's output column j depends on weight column j alone, its row i on src1
-// column i alone).  The host takes this path only when the offsets fit.
-struct LaneMap {
-    uint32_t w_elem;   // the lane's first weight element, from the stage's first
-    uint32_t w_byte;   // its packed byte, w_elem / 2 (w_elem is a multiple of 8)
-    uint32_t b_byte;   // the lane's first src1 value, bytes from the stage's first
-    bool b_whole;      // the tile's src1 values are all in range (uniform; else
-                       // the checked loads of src1, for a ragged last tile of m)
-};
-
-template <int kTileI, bool kSrc1Transposed>
-__device__ __forceinline__ LaneMap lane_map(const FusedArgs &a, int64_t i0, int64_t j0, int t)
-{
-    LaneMap ln;
-    const int col = (t & 15) * 8;
-    const uint32_t col_in = j0 + col < a.n_cols ? static_cast<uint32_t>(col) : 0u;
-    ln.w_elem = static_cast<uint32_t>(t >> 4) * static_cast<uint32_t>(a.n_cols) + col_in;
-    ln.w_byte = ln.w_elem >> 1;
-    constexpr int kB = Shape<kTileI>::kB;
-    const uint32_t ld = static_cast<uint32_t>(a.ld);
-    if constexpr (!kSrc1Transposed) {
-        constexpr int kLanesPerRow = kTileI / kB;
-        const uint32_t ib = static_cast<uint32_t>((t % kLanesPerRow) * kB);
-        ln.b_byte = 4u * (static_cast<uint32_t>(t / kLanesPerRow) * ld + ib);
-        ln.b_whole = i0 + kTileI <= a.m;
-    } else {
-        constexpr int kLanesPerCol = kStage / kB;
-        const uint32_t ic = static_cast<uint32_t>(t / kLanesPerCol);
-        const uint32_t ic_in = i0 + ic < a.m ? ic : 0u;
-        ln.b_byte = 4u * (ic_in * ld + static_cast<uint32_t>((t % kLanesPerCol) * kB));
-        ln.b_whole = true;
-    }
-    return ln;
-}
-
-// A raw buffer over `bytes` bytes from `base`.  A full stage's loads go
-// through buffers whose base is the stage's uniform address, so each load
-// is one scalar base plus the lane's 32-bit offset.
+// A raw buffer over `bytes` bytes from `base`: each load through it is one
+// scalar base plus 32-bit offsets, with no 64-bit address arithmetic.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_buffer(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
@@ -404,75 +317,6 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t buf, uint32_t b
 {
     return __builtin_bit_cast(float,
                               __builtin_amdgcn_raw_buffer_load_b32(buf, byte_offset, extra, 0));
-}
-
-template <int kTileI, bool kSrc1Transposed>
-__device__ __forceinline__ void load_full_stage(const FusedArgs &a, int64_t k0, int64_t k_end,
-                                                int64_t i0, int64_t j0, int t,
-                                                const LaneMap &ln, StageLoad<kTileI> &ld)
-{
-    const int lb = a.log2_block;
-    const uint32_t n_cols = static_cast<uint32_t>(a.n_cols);
-    const int64_t e0 = k0 * a.n_cols + j0;  // a multiple of 8
-    ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(
-        span_buffer(a.packed + (e0 >> 1), kStage / 2 * n_cols), ln.w_byte, 0, 0);
-    // block of the lane's 8 elements, (e0 + w_elem) >> lb: a uniform part bh
-    // and the lane's part c
-    const int64_t bh = e0 >> lb;
-    const uint32_t bl = static_cast<uint32_t>(e0 & ((int64_t{1} << lb) - 1));
-    const uint32_t c = (bl + ln.w_elem) >> lb;
-    const uint32_t c_span = ((kStage * n_cols + 4095u) >> lb) + 1u;
-    ld.code_lo = __builtin_amdgcn_raw_buffer_load_b8(span_buffer(a.scale_codes + bh, c_span), c,
-                                                     0, 0);
-    const uint32_t g =
-        (static_cast<uint32_t>(bh & ((1 << kNestedLog2) - 1)) + c) >> kNestedLog2;
-    const uint32_t g_span = 4u * ((c_span + 255u) / 256u + 1u);
-    ld.absmax_lo = load_f32(span_buffer(a.nested_absmax + (bh >> kNestedLog2), g_span), 4u * g);
-    constexpr int kB = Shape<kTileI>::kB;
-    if (ln.b_whole) {
-        const uint32_t ld_src1 = static_cast<uint32_t>(a.ld);
-        const __amdgpu_buffer_rsrc_t b =
-            kSrc1Transposed
-                ? span_buffer(a.src1 + (i0 * a.ld + k0), 4u * (kTileI * ld_src1 + kStage))
-                : span_buffer(a.src1 + (k0 * a.ld + i0), 4u * (kStage * ld_src1 + kTileI));
-        if constexpr (kB % 4 == 0) {
-            // kB consecutive floats: 16-byte loads (dword alignment suffices).
-            // The whole vector is cast at once: casting its lanes one by one
-            // let this compiler shrink the load to its first dword.
-#pragma unroll
-            for (int q = 0; q < kB; q += 4) {
-                const f32x4 v = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(b, ln.b_byte, 4 * q, 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ld.b[q + e] = v[e];
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < kB; ++q)
-                ld.b[q] = load_f32(b, ln.b_byte, 4 * q);
-        }
-    } else {
-        load_stage_b<kTileI, kSrc1Transposed>(a, k0, k_end, i0, t, ld);
-    }
-}
-
-template <int kTileI, bool kSrc1Transposed>
-__device__ __forceinline__ void decode_full_stage(const FusedArgs &a, int t,
-                                                  const StageLoad<kTileI> &ld,
-                                                  const float *lds_scb, const float *lds_cb4,
-                                                  const f32x2 *lds_pair,
-                                                  float (*lds_w)[kLdsW],
-                                                  float (*lds_b)[Shape<kTileI>::kLdsB])
-{
-    const int row = t >> 4, col = (t & 15) * 8;
-    const float s = block_scale(lds_scb[ld.code_lo], ld.absmax_lo, a.offset);
-    float v[8];
-    decode8<Shape<kTileI>::kPairTable>(ld.packed4, s, lds_cb4, lds_pair, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        lds_w[row][col + q] = v[q];
-    store_stage_b<kTileI, kSrc1Transposed>(t, ld, lds_b);
 }
 
 // The MFMAs of one stage: acc[bi][bj] += A(i block bi) x W(j block bj) over
@@ -526,7 +370,7 @@ __device__ __forceinline__ void mma_stage(
 // into the other buffer, so one barrier per stage suffices.  The stage loop
 // is unrolled by two, so that each step's LDS buffers are known at compile
 // time and every LDS address is a lane-constant register plus an immediate.
-template <int kTileI, bool kSrc1Transposed, bool kAligned8>
+template <int kTileI, bool kSrc1Transposed>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Shape<kTileI>::kMinWaves)))
 void out_prod_fused_kernel(FusedArgs a)
 {
@@ -535,7 +379,6 @@ void out_prod_fused_kernel(FusedArgs a)
     __shared__ float lds_b[2][kStage][S::kLdsB];
     __shared__ float lds_scb[256];
     __shared__ float lds_cb4[16];
-    __shared__ f32x2 lds_pair[S::kPairTable ? 256 : 1];  // (entry of low nibble, high nibble)
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -550,8 +393,6 @@ void out_prod_fused_kernel(FusedArgs a)
     lds_scb[t] = a.scale_codebook[t];
     if (t < 16)
         lds_cb4[t] = a.codebook4[t];
-    if constexpr (S::kPairTable)
-        lds_pair[t] = f32x2{a.codebook4[t & 15], a.codebook4[t >> 4]};
 
     const int wi = wave % S::kWavesI, wj = wave / S::kWavesI;
     const int kl = lane / S::kBlk, cl = lane % S::kBlk;
@@ -564,43 +405,20 @@ void out_prod_fused_kernel(FusedArgs a)
             for (int bj = 0; bj < S::kBlocksJ; ++bj)
                 acc[q][bi][bj] = typename S::Acc{};
 
-    // stage s holds rows k_begin + kStage * s ..; the first n_full stages are
-    // full and, on the aligned path when the host allows it, take the
-    // unchecked loads
-    // (stage counts are below 2^31: the host caps the rows of a split)
+    // stage s holds rows k_begin + kStage * s .. (stage counts are below
+    // 2^31: the host caps the rows of a split)
     const int64_t rows = k_end - k_begin;  // > 0
     const int n_stages =
         __builtin_amdgcn_readfirstlane(static_cast<int>((rows + kStage - 1) >> kLog2Stage));
-    const int n_full = kAligned8 && a.full_stages
-                           ? __builtin_amdgcn_readfirstlane(static_cast<int>(rows >> kLog2Stage))
-                           : 0;
-    LaneMap ln{};
-    if constexpr (kAligned8)
-        ln = lane_map<kTileI, kSrc1Transposed>(a, i0, j0, t);
 
     StageLoad<kTileI> ld;
     const auto load = [&](int s) {
-        const int64_t k0 = k_begin + kStage * s;
-        if constexpr (kAligned8) {
-            if (s < n_full) {
-                load_full_stage<kTileI, kSrc1Transposed>(a, k0, k_end, i0, j0, t, ln, ld);
-                return;
-            }
-        }
-        load_stage<kTileI, kSrc1Transposed, kAligned8>(a, k0, k_end, i0, j0, t, ld);
+        load_stage<kTileI, kSrc1Transposed>(a, k_begin + kStage * s, k_end, i0, j0, t, ld);
     };
     const auto decode = [&](int s, auto buffer) {
         constexpr int q = decltype(buffer)::value;
-        if constexpr (kAligned8) {
-            if (s < n_full) {
-                decode_full_stage<kTileI, kSrc1Transposed>(a, t, ld, lds_scb, lds_cb4, lds_pair,
-                                                           lds_w[q], lds_b[q]);
-                return;
-            }
-        }
-        decode_stage<kTileI, kSrc1Transposed, kAligned8>(a, k_begin + kStage * s, k_end, j0, t,
-                                                         ld, lds_scb, lds_cb4, lds_pair,
-                                                         lds_w[q], lds_b[q]);
+        decode_stage<kTileI, kSrc1Transposed>(a, k_begin + kStage * s, k_end, j0, t, ld,
+                                              lds_scb, lds_cb4, lds_w[q], lds_b[q]);
     };
     // one step: the MFMAs of stage s (in buffer q), then stage s + 1 decoded
     // into the other buffer and the loads of stage s + 2 issued
@@ -819,8 +637,7 @@ void out_prod_direct_kernel(FusedArgs a)
         for (int bj = 0; bj < 8; ++bj)
             acc[bi][bj] = f32x4{};
     const auto decode = [&](const DirectLoad<kBI> &ld, float (&v)[8]) {
-        decode8<true>(ld.packed4, block_scale(lds_scb[ld.code], ld.absmax, a.offset), nullptr,
-                      lds_pair, v);
+        decode8(ld.packed4, block_scale(lds_scb[ld.code], ld.absmax, a.offset), lds_pair, v);
     };
     const auto full_step = [&](const DirectLoad<kBI> &ld) {
         float v[8];
@@ -1059,28 +876,20 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch: on the aligned path the direct kernel for m <= 64
-// (16, 32, 48 or 64 rows per tile); 16-row tiles for decode-sized m on the
-// byte path; else the width of least tile_cost.
-// `variant` (0..27) indexes the kernel for the occupancy cache.
+// The kernel for a launch (see plan_for).  `variant` (0..27) indexes the
+// kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
     int tile_i;
     int variant;
-    bool direct;  // out_prod_direct_kernel (full steps), else the staged kernel (full stages)
+    bool direct;  // out_prod_direct_kernel (its full steps may take unchecked loads)
 };
 
-template <int kTileI, bool kSrc1Transposed>
-const void *kernel_for(bool aligned8)
+template <int kTileI>
+const void *staged_kernel(bool transposed)
 {
-    if constexpr (kTileI == 16)  // the aligned path of m <= 64 is the direct kernel's
-        return reinterpret_cast<const void *>(
-            &out_prod_fused_kernel<16, kSrc1Transposed, false>);
-    else
-        return aligned8
-               ? reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, kSrc1Transposed, true>)
-               : reinterpret_cast<const void *>(
-                     &out_prod_fused_kernel<kTileI, kSrc1Transposed, false>);
+    return transposed ? reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, true>)
+                      : reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, false>);
 }
 
 // Relative work per dst row of each i-tile width, measured on the output head
@@ -1102,11 +911,15 @@ const void *direct_kernel(bool transposed)
                : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kQuad, false>);
 }
 
+// The kernel for m dst rows.  The aligned path takes the direct kernel's
+// tiles: the 4-row sets for m <= 8, then 16, 32, 48 or 64 rows (m > 64
+// repeats the 64-row tile over the rows; the call splits such m into whole
+// 64-row tiles and a smaller rest, see row_ranges).  The byte path takes the
+// staged kernel.
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
-    const int sub = (transposed ? 2 : 0) + (aligned8 ? 1 : 0);
-    if (m <= 64 && aligned8) {
-        const int t = transposed ? 1 : 0;
+    const int t = transposed ? 1 : 0;
+    if (aligned8) {
         if (m <= 4)
             return {direct_kernel<1, true>(transposed), 4, 24 + t, true};
         if (m <= 8)
@@ -1120,19 +933,16 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
         return {direct_kernel<4>(transposed), 64, 20 + t, true};
     }
     if (m <= 16)
-        return {transposed ? kernel_for<16, true>(false) : kernel_for<16, false>(false), 16, sub, false};
+        return {staged_kernel<16>(transposed), 16, 2 * t, false};
     int64_t best = 64;
     for (const int64_t w : {128, 256})
         if (tile_cost(m, w) < tile_cost(m, best))
             best = w;
     if (best == 256)
-        return {transposed ? kernel_for<256, true>(aligned8) : kernel_for<256, false>(aligned8),
-                256, 12 + sub, false};
+        return {staged_kernel<256>(transposed), 256, 12 + 2 * t, false};
     if (best == 128)
-        return {transposed ? kernel_for<128, true>(aligned8) : kernel_for<128, false>(aligned8),
-                128, 8 + sub, false};
-    return {transposed ? kernel_for<64, true>(aligned8) : kernel_for<64, false>(aligned8), 64,
-            4 + sub, false};
+        return {staged_kernel<128>(transposed), 128, 8 + 2 * t, false};
+    return {staged_kernel<64>(transposed), 64, 4 + 2 * t, false};
 }
 
 constexpr int kVariants = 28;
@@ -1186,21 +996,6 @@ int64_t rows_per_split(int64_t n_rows, int64_t tiles, int64_t resident, int64_t 
     return ceil_div(ceil_div(n_rows, splits), kStage) * kStage;
 }
 
-// Whether full stages may take the unchecked loads: the lane-constant offsets
-// of LaneMap and the block arithmetic of load_full_stage stay below 2^32
-// (weights: kStage rows of n_cols elements plus a block offset under 4096;
-// src1: kStage rows, or tile_i columns when transposed, of ld floats).
-bool full_stages_fit(int64_t n_cols, int64_t ld, int tile_i, bool transposed)
-{
-    constexpr int64_t k32 = int64_t{1} << 32;
-    if (n_cols >= k32 / kStage || kStage * n_cols + 4096 >= k32)
-        return false;
-    const int64_t rows = transposed ? tile_i : kStage;
-    if (ld >= k32 / 4 / rows)
-        return false;
-    return 4 * (rows * ld + tile_i + kStage) < k32;
-}
-
 // Whether the direct kernel's full steps may address a split of `rows` rows
 // (at most) from one base per array with 32-bit offsets: its rows * n_cols
 // weight elements plus a block offset under 4096 (and the lanes' columns),
@@ -1214,6 +1009,35 @@ bool direct_split_fits(int64_t rows, int64_t n_cols, int64_t ld, int tile_i, boo
         return false;
     return transposed ? ld < kFloats / tile_i && tile_i * ld + rows < kFloats
                       : ld < kFloats / rows && rows * ld + tile_i < kFloats;
+}
+
+// A call's dst rows are covered by at most two ranges, each with its own plan
+// and launches: dst row i depends on src1 column i alone, so a range is the
+// same operation on a column slice of src1.  On the aligned path m > 64
+// takes whole 64-row direct tiles for its first 64 * floor(m / 64) rows and
+// the best smaller tile for the rest.  The 64-row direct tile costs no more
+// per dst row than the staged kernel's 256-row tile (output head, row-major
+// src1: 1.58 against 1.67 ms at m = 128, 6.19 against 6.41 ms at m = 512,
+// 12.09 against 12.79 ms at m = 1024), and the rest pays for its own rows
+// rather than for a padded wide tile (m = 192: 2.37 against 3.58 ms).
+struct RowRange {
+    int64_t i_begin;  // first dst row (src1 column) of the range
+    int64_t m;        // its dst rows
+    Plan plan;
+};
+
+int row_ranges(int64_t m, bool transposed, bool aligned8, RowRange (&r)[2])
+{
+    if (aligned8 && m > 64) {
+        const int64_t whole = m / 64 * 64;
+        r[0] = {0, whole, plan_for(64, transposed, true)};
+        if (whole == m)
+            return 1;
+        r[1] = {whole, m - whole, plan_for(m - whole, transposed, true)};
+        return 2;
+    }
+    r[0] = {0, m, plan_for(m, transposed, aligned8)};
+    return 1;
 }
 
 dq4_status_t grid_size(int64_t count, int device, uint32_t *grid)
@@ -1237,17 +1061,25 @@ int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess)
         return 0;
-    // the largest split any variant of the kernel would take for this shape
-    int64_t splits = 1;
+    // the largest partials any variant of the kernels would write for this
+    // shape (the row ranges of a call use the workspace one after the other)
+    int64_t bytes = 0;
     for (int v = 0; v < 4; ++v) {
-        const dq4::Plan plan = dq4::plan_for(m, (v & 1) != 0, (v & 2) != 0);
-        const int64_t tiles = dq4::ceil_div(m, plan.tile_i) * dq4::ceil_div(n_cols, dq4::kTileJ);
-        const int64_t resident =
-            int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan, device);
-        const int64_t rps = dq4::rows_per_split(n_rows, tiles, resident, dq4::kMaxSplits);
-        splits = std::max(splits, dq4::ceil_div(n_rows, rps));
+        dq4::RowRange ranges[2];
+        const int n_ranges = dq4::row_ranges(m, (v & 1) != 0, (v & 2) != 0, ranges);
+        for (int k = 0; k < n_ranges; ++k) {
+            const dq4::RowRange &r = ranges[k];
+            const int64_t tiles =
+                dq4::ceil_div(r.m, r.plan.tile_i) * dq4::ceil_div(n_cols, dq4::kTileJ);
+            const int64_t resident =
+                int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(r.plan, device);
+            const int64_t rps = dq4::rows_per_split(n_rows, tiles, resident, dq4::kMaxSplits);
+            const int64_t splits = dq4::ceil_div(n_rows, rps);
+            if (splits > 1)
+                bytes = std::max(bytes, splits * r.m * n_cols * 4);
+        }
     }
-    return splits > 1 ? splits * m * n_cols * 4 : 0;
+    return bytes;
 }
 
 dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_codes,
@@ -1272,18 +1104,22 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
         return DQ4_EINVAL;
     const int64_t count = m * n_cols;
     const bool aligned8 = n_cols % 8 == 0 && reinterpret_cast<uintptr_t>(packed) % 4 == 0;
-    const dq4::Plan plan = dq4::plan_for(m, src1_transposed != 0, aligned8);
-    const int64_t tiles_i = dq4::ceil_div(m, plan.tile_i);
+    const bool transposed = src1_transposed != 0;
+    dq4::RowRange ranges[2];
+    const int n_ranges = dq4::row_ranges(m, transposed, aligned8, ranges);
     const int64_t tiles_j = dq4::ceil_div(n_cols, dq4::kTileJ);
     if (n_rows > 0) {
         if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 || !src1)
             return DQ4_EINVAL;
-        if (src1_transposed ? ld_src1 < n_rows : ld_src1 < m)
+        if (transposed ? ld_src1 < n_rows : ld_src1 < m)
             return DQ4_EINVAL;
         if (workspace_bytes > 0 && !workspace)
             return DQ4_EINVAL;
-        if (tiles_i > 0x7FFFFFFF || tiles_j > 0x7FFFFFFF || tiles_i * tiles_j > 0x7FFFFFFF)
-            return DQ4_EUNSUPPORTED;
+        for (int k = 0; k < n_ranges; ++k) {
+            const int64_t tiles_i = dq4::ceil_div(ranges[k].m, ranges[k].plan.tile_i);
+            if (tiles_i > 0x7FFFFFFF || tiles_j > 0x7FFFFFFF || tiles_i * tiles_j > 0x7FFFFFFF)
+                return DQ4_EUNSUPPORTED;
+        }
     }
     int device = 0;
     hipError_t e = hipGetDevice(&device);
@@ -1300,41 +1136,59 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
                             dim3(grid), dim3(dq4::kThreads), params, 0, s);
         return e == hipSuccess ? DQ4_OK : dq4::hip_failed(e);
     }
-    const int64_t max_partials = workspace_bytes / 4 / count;
-    const int64_t resident =
-        int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan, device);
-    const int64_t rps = dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
-    const int64_t splits = dq4::ceil_div(n_rows, rps);
-    const int64_t groups = splits * tiles_i * tiles_j;
-    if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kStage) > 0x7FFFFFFF)
-        return DQ4_EUNSUPPORTED;  // the kernel counts a split's stages in 32 bits
 
-    const bool full =
-        aligned8 && (plan.direct ? dq4::direct_split_fits(rps, n_cols, ld_src1, plan.tile_i,
-                                                         src1_transposed != 0)
-                                 : dq4::full_stages_fit(n_cols, ld_src1, plan.tile_i,
-                                                        src1_transposed != 0));
-    dq4::FusedArgs a{packed, scale_codes, nested_absmax, scale_codebook, codebook4, src1,
-                     splits > 1 ? workspace : dst, n_rows, n_cols, m, ld_src1, rps, offset,
-                     log2_block, static_cast<int>(tiles_i), static_cast<int>(tiles_j),
-                     full ? 1 : 0};
-    void *params[] = {&a};
-    e = hipLaunchKernel(plan.kernel, dim3(static_cast<uint32_t>(groups)), dim3(dq4::kThreads),
-                        params, 0, s);
-    if (e != hipSuccess)
-        return dq4::hip_failed(e);
-    if (splits > 1) {
-        uint32_t grid = 0;
-        dq4::grid_size(count, device, &grid);
-        const float *p = workspace;
-        float *d = dst;
-        int64_t c = count;
-        int sp = static_cast<int>(splits);
-        void *rparams[] = {&p, &d, &c, &sp};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4::out_prod_reduce_kernel),
-                            dim3(grid), dim3(dq4::kThreads), rparams, 0, s);
+    // every range's launch is set up (and checked) before the first is enqueued
+    struct Launch {
+        dq4::FusedArgs args;
+        int64_t groups, splits, count;
+        float *dst;  // the range's first dst row
+    } launches[2];
+    for (int k = 0; k < n_ranges; ++k) {
+        const dq4::RowRange &r = ranges[k];
+        const dq4::Plan &plan = r.plan;
+        const int64_t tiles_i = dq4::ceil_div(r.m, plan.tile_i);
+        const int64_t r_count = r.m * n_cols;
+        const int64_t max_partials = workspace_bytes / 4 / r_count;
+        const int64_t resident =
+            int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(plan, device);
+        const int64_t rps =
+            dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
+        const int64_t splits = dq4::ceil_div(n_rows, rps);
+        const int64_t groups = splits * tiles_i * tiles_j;
+        if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kStage) > 0x7FFFFFFF)
+            return DQ4_EUNSUPPORTED;  // the kernel counts a split's stages in 32 bits
+        const bool full = plan.direct && dq4::direct_split_fits(rps, n_cols, ld_src1,
+                                                                 plan.tile_i, transposed);
+        float *r_dst = dst + r.i_begin * n_cols;
+        const float *r_src1 = transposed ? src1 + r.i_begin * ld_src1 : src1 + r.i_begin;
+        launches[k] = {{packed, scale_codes, nested_absmax, scale_codebook, codebook4, r_src1,
+                        splits > 1 ? workspace : r_dst, n_rows, n_cols, r.m, ld_src1, rps,
+                        offset, log2_block, static_cast<int>(tiles_i),
+                        static_cast<int>(tiles_j), full ? 1 : 0},
+                       groups, splits, r_count, r_dst};
+    }
+    // the ranges run one after the other on the stream, so the second reuses
+    // the workspace once the first range's reduction has read it
+    for (int k = 0; k < n_ranges; ++k) {
+        Launch &l = launches[k];
+        void *params[] = {&l.args};
+        e = hipLaunchKernel(ranges[k].plan.kernel, dim3(static_cast<uint32_t>(l.groups)),
+                            dim3(dq4::kThreads), params, 0, s);
         if (e != hipSuccess)
             return dq4::hip_failed(e);
+        if (l.splits > 1) {
+            uint32_t grid = 0;
+            dq4::grid_size(l.count, device, &grid);
+            const float *p = workspace;
+            float *d = l.dst;
+            int64_t c = l.count;
+            int sp = static_cast<int>(l.splits);
+            void *rparams[] = {&p, &d, &c, &sp};
+            e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4::out_prod_reduce_kernel),
+                                dim3(grid), dim3(dq4::kThreads), rparams, 0, s);
+            if (e != hipSuccess)
+                return dq4::hip_failed(e);
+        }
     }
     return DQ4_OK;
 }

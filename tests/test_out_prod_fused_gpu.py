@@ -68,11 +68,15 @@ DECODE_LAYOUTS = [
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("m", [300, 150, 70, 16, 5])
 def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
-    """Every i-tile width, each with a ragged last tile: m = 300 takes five
-    64-row tiles, m = 150 one 256-row tile, m = 70 one 128-row tile (the
-    widths the kernel's cost rule picks for them); m = 16 and 5 the 16-row
-    tiles of the 16 x 16 x 4 matrix instruction, full and ragged.  Columns
-    select weight rows with repeats when m exceeds the row count."""
+    """Every tile, each with a ragged last tile.  On the byte-path layouts
+    (odd widths) the staged kernel: m = 300 takes five 64-row tiles, m = 150
+    one 256-row tile, m = 70 one 128-row tile (the widths its cost rule picks
+    for them), m = 16 and 5 the 16-row tile, full and ragged.  On the aligned
+    layouts the direct kernel: whole 64-row tiles and the rest in a smaller
+    tile (300 = 4 x 64 + 44 in a 48-row tile, 150 = 2 x 64 + 22 in a 32-row
+    tile, 70 = 64 + 6 in an 8-row set), m = 16 the 16-row tile and m = 5 the
+    8-row set.  Columns select weight rows with repeats when m exceeds the
+    row count."""
     n_rows, n_cols, bs, fmt = layout
     x = inputs.make_inputs(n_rows * n_cols, bs, fmt, -0.1, seed=n_rows * 7 + n_cols,
                            n_rows=n_rows, n_cols=n_cols)
@@ -206,14 +210,15 @@ def test_direct_tiles_steps_and_splits(n_rows, transposed):
             assert bad.size == 0, f"m={m}: first mismatch at (i, j) = {bad[0]}"
 
 
-def test_staged_tile_keeps_checked_loads_past_32_bit_offsets():
-    """The staged kernel's counterpart of the test above: m = 65 takes the
-    128-row staged tile, and a transposed src1 whose leading dimension puts
-    the tile's 128 columns more than 2^32 bytes apart keeps every stage on
-    the checked loads.  Bits equal those of a compact src1, and the rows are
-    the oracle's."""
+def test_row_ranges_keep_checked_loads_past_32_bit_offsets():
+    """m = 65 takes a 64-row direct tile and, for the last row, a 4-row set.
+    A transposed src1 whose leading dimension puts the 64-row tile's columns
+    more than 2^32 bytes apart keeps that tile's steps on the checked loads,
+    while the 4-row set, whose columns span 2^28 bytes, takes the unchecked
+    ones.  Bits equal those of a compact src1, and the rows are the
+    oracle's."""
     n_rows, n_cols, m = 16 + 5, 256, 65
-    ld = (1 << 23) + 16
+    ld = (1 << 24) + 16
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.01, seed=779, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
@@ -242,8 +247,8 @@ def test_infinite_src1_reaches_only_its_own_products(m, transposed):
     elsewhere.  One +inf per src1 column at a random row (the rows cover many
     splits); the NaN and infinity pattern of dst, and the infinities' signs,
     equal those of inf * W[r][j] added to the finite part, and every other
-    element is finite (direct tiles at m = 3, 12, 16 and 48, the staged tile
-    at m = 100)."""
+    element is finite (direct tiles at m = 3, 12, 16 and 48; at m = 100 a
+    64-row tile and a 48-row tile for the other 36 rows)."""
     n_rows, n_cols = 4099, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=780 + m, n_rows=n_rows,
                            n_cols=n_cols)
@@ -309,12 +314,13 @@ def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
                                           f"workspace={'preferred' if ws is None else 'none'}")
 
 
-@pytest.mark.parametrize("m", [4, 8, 16, 32, 48, 64, 512])
+@pytest.mark.parametrize("m", [4, 8, 16, 32, 48, 64, 100, 512])
 def test_selection_output_head_is_bit_exact(m):
     """Selection-matrix src1 over the 151 936 x 5 376 output head, both
     orientations, at each tile of the direct kernel (4, 8, 16, 32, 48 and 64
-    rows) and the staged 256-row tile: every row split is selected; dst
-    equals the weight rows exactly."""
+    rows), at m = 100 (a 64-row tile, then a 48-row tile for the other 36
+    rows) and at m = 512 (eight 64-row tiles): every row split is selected;
+    dst equals the weight rows exactly."""
     wl = inputs.OUTPUT_HEAD
     x = cases.output_head_weight()
     dev = dq4.to_device(x)
@@ -351,14 +357,17 @@ def test_output_head_both_orientations_and_against_the_blocked_route(m):
                         "fused vs blocked", factor=2.0)
 
 
+@pytest.mark.parametrize("n_cols", [200, 201])
 @pytest.mark.parametrize("m", [150, 300])
-def test_ragged_tiles_every_split_and_determinism(m):
-    """m = 150 (one ragged 256-row i-tile) and m = 300 (five 64-row i-tiles,
-    the last ragged), n_cols = 200 (two j-tiles, blocks of 64 spanning rows),
+def test_ragged_tiles_every_split_and_determinism(m, n_cols):
+    """m = 150 and 300 with random src1 on both paths: n_cols = 200 (the
+    aligned path: 150 = 2 x 64 + 22 rows in a 32-row tile, 300 = 4 x 64 + 44
+    in a 48-row tile) and n_cols = 201 (the byte path: one ragged 256-row
+    tile, five 64-row tiles), two j-tiles with blocks of 64 spanning rows;
     with no workspace (one split), a workspace of two partials, and the
     preferred one; each result is within the bound, and a repeated call gives
     the same bits."""
-    n_rows, n_cols = 3000, 200
+    n_rows = 3000
     x = inputs.make_inputs(n_rows * n_cols, 64, "fp4", 0.1, seed=3000, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
