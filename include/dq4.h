@@ -265,10 +265,15 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
  * The summation order differs from dq4_out_prod_rows; both are within the
  * FP32 summation bound of the exact sum.
  *
+ * The dst rows may be computed in two ranges one after the other (dst row i
+ * depends on src1 column i alone): on the aligned path (n_cols % 8 == 0,
+ * packed 4-byte aligned) m > 64 takes whole 64-row tiles, then the rest.
+ *
  * workspace: optional caller-owned device memory for partial sums.  When the
- * dst tiles alone cannot fill the GPU, the rows are split and each split's
- * partial dst (m * n_cols FP32) goes to the workspace, then one more kernel
- * adds the partials in split order into dst.  The number of splits is the
+ * dst tiles alone cannot fill the GPU, the rows r are split and each split's
+ * partial of the range's dst rows (at most m * n_cols FP32) goes to the
+ * workspace, then one more kernel adds the partials in split order into dst;
+ * the ranges reuse the workspace in turn.  The number of splits is the
  * largest of those the workspace holds up to the preferred count
  * (dq4_out_prod_fused_workspace_bytes); with workspace_bytes == 0 there is
  * one split and dst is written directly.  The workspace changes speed only;
