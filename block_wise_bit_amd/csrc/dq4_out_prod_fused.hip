@@ -476,10 +476,10 @@ void out_prod_fused_kernel(FusedArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Direct tiles for small m (m <= 64) on the aligned path.  With few dst rows
-// each decoded weight feeds only m products, and staging the weights through
-// LDS (a write and a read per element) made the LDS the limit at m = 16.
-// Here each lane decodes its packed dword straight into the operand layout of
+// Direct tiles on the aligned path, up to 64 dst rows each (a wider m repeats
+// the tile over the rows).  With few dst rows each decoded weight feeds only a
+// tile's products, and staging the weights through LDS (a write and a read
+// per element) made the LDS the limit at m = 16.  Here each lane decodes its packed dword straight into the operand layout of
 // v_mfma_f32_16x16x4_f32: a step covers 4 weight rows (the instruction's k)
 // and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
 // columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
@@ -892,10 +892,10 @@ const void *staged_kernel(bool transposed)
                       : reinterpret_cast<const void *>(&out_prod_fused_kernel<kTileI, false>);
 }
 
-// Relative work per dst row of each i-tile width, measured on the output head
-// with m a multiple of the width (FP32 TFLOP/s 128 / 109 / 93 at widths
-// 256 / 128 / 64): the decode cost of a stage is shared by more rows in a
-// wider tile.  A ragged m pays for its padded rows, so the width that
+// Relative work per dst row of each staged i-tile width, measured on the
+// output head with m a multiple of the width (FP32 TFLOP/s 128 / 109 / 93 at
+// widths 256 / 128 / 64): the decode cost of a stage is shared by more rows
+// in a wider tile.  A ragged m pays for its padded rows, so the width that
 // minimizes padded rows x relative cost wins.
 double tile_cost(int64_t m, int64_t tile_i)
 {
