@@ -479,19 +479,19 @@ void out_prod_fused_kernel(FusedArgs a)
 // Direct tiles on the aligned path, up to 64 dst rows each (a wider m repeats
 // the tile over the rows).  With few dst rows each decoded weight feeds only a
 // tile's products, and staging the weights through LDS (a write and a read
-// per element) made the LDS the limit at m = 16.  Here each lane decodes its packed dword straight into the operand layout of
-// v_mfma_f32_16x16x4_f32: a step covers 4 weight rows (the instruction's k)
-// and the tile's 128 columns as 8 blocks of 16, lane l taking row l / 16 and
-// columns 8 (l % 16) .. + 7, so that its 8 decoded values are its operands of
-// the 8 blocks (block bj's column c is weight column 8c + bj).  The tile's
-// 16 * kBI dst rows (kBI = 1 .. 4) are kBI blocks of 16 in the same way
-// (block bi's row c is dst row kBI c + bi), so a lane's src1 operands of one
-// step are kBI consecutive floats of one src1 row, loaded straight from
-// global memory.  The store undoes both permutations.  The 4 waves of a
-// workgroup take every fourth step of the split's rows and add their partial
-// tiles at the end in a fixed order ((w0 + w2) + (w1 + w3)), so the result
-// stays deterministic.  Only the codebooks live in LDS during the main loop,
-// which has no barrier.
+// per element) made the LDS the limit at m = 16.  Here each lane decodes its
+// packed dword straight into the operand layout of v_mfma_f32_16x16x4_f32: a
+// step covers 4 weight rows (the instruction's k) and the tile's 128 columns
+// as 8 blocks of 16, lane l taking row l / 16 and columns 8 (l % 16) .. + 7,
+// so that its 8 decoded values are its operands of the 8 blocks (block bj's
+// column c is weight column 8c + bj).  The tile's 16 * kBI dst rows (kBI =
+// 1 .. 4) are kBI blocks of 16 in the same way (block bi's row c is dst row
+// kBI c + bi), so a lane's src1 operands of one step are kBI consecutive
+// floats of one src1 row, loaded straight from global memory.  The store
+// undoes both permutations.  The 4 waves of a workgroup take every fourth
+// step of the split's rows and add their partial tiles at the end in a fixed
+// order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.  Only the
+// codebooks live in LDS during the main loop, which has no barrier.
 //
 // With kQuad, for m <= 8, the same steps feed v_mfma_f32_4x4x1_16b_f32
 // instead: 16 independent 4 x 4 blocks of k = 1, block b = l / 4 made of
@@ -503,9 +503,11 @@ void out_prod_fused_kernel(FusedArgs a)
 // the four weight rows of a step hold partial sums of the same dst elements;
 // they are added across lanes at the end, (g0 + g1) + (g2 + g3) over the lane
 // groups l / 16.  The instruction does a quarter of the 16 x 16 x 4 one's
-// products in about half its time (per call on the output head: 0.19 ms at
-// m <= 4 and 0.25 ms at m <= 8 against 0.28 ms for the 16-row tile, and
-// 0.33 ms with three sets, so m <= 12 keeps the 16-row tile).
+// products in a quarter of its matrix-pipe time (8 cycles against 32, by
+// counters), but the decode's vector instructions, which do not overlap FP32
+// matrix instructions, are the same per step: on the output head m <= 4
+// takes 0.16 ms and m <= 8 0.22 ms against 0.26 ms for the 16-row tile, and
+// three sets (m <= 12) measured slower than the 16-row tile, which keeps them.
 constexpr int kDirectK = 4;   // weight rows per step (n_steps uses >> 2)
 
 template <int kBI>
