@@ -98,14 +98,16 @@ def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
 
 
 @pytest.mark.parametrize("transposed", [False, True])
-@pytest.mark.parametrize("m", [5, 16, 70, 150])
+@pytest.mark.parametrize("m", [3, 5, 16, 70, 150])
 def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
-    """The kernel's full stages load without bounds checks: lanes past n_cols
-    or past m read in-range elements whose products only reach dst elements
-    that are never stored.  Here src1's padding (ld > m, or ld > n_rows when
-    transposed) holds NaN, the weight's last 128-column tile is ragged and its
-    last 16-row stage partial; a NaN that reached a stored element's sum
-    would show, so dst row i must equal the oracle's weight row sel[i]."""
+    """The direct kernel's full steps load without bounds checks: lanes past
+    n_cols or past m read in-range elements whose products only reach dst
+    elements that are never stored.  Here src1's padding (ld > m, or ld >
+    n_rows when transposed) holds NaN, the weight's last 128-column tile is
+    ragged and its last 4-row step partial; a NaN that reached a stored
+    element's sum would show, so dst row i must equal the oracle's weight row
+    sel[i] (the 4- and 8-row sets, the 16-row tile, and 64-row tiles with a
+    smaller tile for the rest)."""
     n_rows, n_cols = 16 * 37 + 5, 400
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=777, n_rows=n_rows,
                            n_cols=n_cols)
