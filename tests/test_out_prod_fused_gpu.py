@@ -129,6 +129,39 @@ def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
         assert bad.size == 0, f"first mismatch at (i, j) = {bad[0]}: {y[tuple(bad[0])]!r}"
 
 
+@pytest.mark.parametrize("transposed", [False, True])
+def test_packed_pointer_off_a_dword_takes_the_byte_path(transposed):
+    """A weight whose rows are 8-aligned (n_cols = 384) but whose packed bytes
+    start 1, 2 or 3 bytes past a 4-byte boundary cannot be read one dword per
+    lane, so the call takes the staged byte path; with a selection-matrix
+    src1 dst row i equals the oracle's weight row sel[i] at m = 5, 16 and 70,
+    as the same call on the aligned copy does."""
+    n_rows, n_cols = 131, 384
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.04, seed=783, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
+    nbytes = dev["packed"].numel()
+    for shift in (1, 2, 3):
+        buf = torch.zeros(nbytes + 8, dtype=torch.uint8, device="cuda")
+        buf[shift:shift + nbytes].copy_(dev["packed"])
+        moved = dict(dev, packed=buf[shift:shift + nbytes])
+        assert moved["packed"].data_ptr() % 4 == shift
+        for m in (5, 16, 70):
+            rng = np.random.Generator(np.random.PCG64(m * 10 + shift))
+            sel = rng.integers(0, n_rows, size=m)
+            b = np.zeros((n_rows, m), np.float32)
+            b[sel, np.arange(m)] = 1.0
+            kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64,
+                      src1=_src1(b, transposed), src1_transposed=transposed)
+            y = dq4.dq4_out_prod_fused(**moved, **kw).cpu().numpy()
+            bad = np.argwhere(y != w[sel])
+            assert bad.size == 0, f"shift {shift} m={m}: first mismatch at (i, j) = {bad[0]}"
+            y_aligned = dq4.dq4_out_prod_fused(**dev, **kw).cpu().numpy()
+            assert np.array_equal(y, y_aligned), f"shift {shift} m={m}"
+        del buf, moved
+
+
 def test_leading_dimension_past_32_bit_offsets_keeps_the_checked_loads():
     """A transposed src1 whose leading dimension puts the 4 columns of the
     m = 2 tile more than 2^32 bytes apart: the unchecked steps' 32-bit
