@@ -493,7 +493,8 @@ void out_prod_fused_kernel(FusedArgs a)
 // order ((w0 + w2) + (w1 + w3)), so the result stays deterministic.  Only the
 // codebooks live in LDS during the main loop, which has no barrier.
 //
-// With kQuad, for m <= 8, the same steps feed v_mfma_f32_4x4x1_16b_f32
+// kMode selects how a step's products are summed.  Mode 0 is the above.
+// In mode 1 (4-row sets), for m <= 8, the same steps feed v_mfma_f32_4x4x1_16b_f32
 // instead: 16 independent 4 x 4 blocks of k = 1, block b = l / 4 made of
 // lanes 4b .. 4b + 3.  The weight operand keeps its place (lane l's value q
 // is column j = l % 4 of its block), and the src1 operand of lane l is src1
@@ -508,6 +509,14 @@ void out_prod_fused_kernel(FusedArgs a)
 // matrix instructions, are the same per step: on the output head m <= 4
 // takes 0.16 ms and m <= 8 0.22 ms against 0.26 ms for the 16-row tile, and
 // three sets (m <= 12) measured slower than the 16-row tile, which keeps them.
+//
+// Mode 2, for m == 1, sums on the vector unit: each lane adds b * W for its
+// 8 weights with fused multiply-adds into 8 accumulators, and the lane groups
+// and waves are added as in mode 1.  Each weight W is still its own rounded
+// product fl32(codebook4[k] * scale); only the accumulation is fused, as it
+// is inside the matrix instructions.  The step's 8 FMAs issue in 32 cycles
+// against the 64 of its 8 matrix instructions (0.13 against 0.16 ms on the
+// output head); from m = 2 on they would cost as much.
 constexpr int kDirectK = 4;   // weight rows per step (n_steps uses >> 2)
 
 template <int kBI>
@@ -518,33 +527,42 @@ struct DirectLoad {
     float b[kBI];
 };
 
-template <int kBI, bool kQuad>
+template <int kBI, int kMode>
 struct Direct {
-    static constexpr int kRows = (kQuad ? 4 : 16) * kBI;  // dst rows of the tile
-    static constexpr int kMinWaves = kBI >= 3 && !kQuad ? 2 : 1;
+    static constexpr bool kQuad = kMode == 1;  // 4-row sets on the 4 x 4 x 1 instruction
+    static constexpr bool kVec = kMode == 2;   // one dst row on the vector unit
+    static constexpr int kRows = kVec ? 1 : (kQuad ? 4 : 16) * kBI;  // dst rows of the tile
+    static constexpr int kAccV = kVec ? 1 : 4;  // accumulator values per block and lane
+    static constexpr int kMinWaves = kBI >= 3 && kMode == 0 ? 2 : 1;
 
     // the tile row of the lane's src1 operand of block (or set) bi
     static __device__ __forceinline__ uint32_t src1_row(int lane, int bi)
     {
+        if constexpr (kVec)
+            return 0u;
         return kQuad ? static_cast<uint32_t>(4 * bi + (lane & 3))
                      : static_cast<uint32_t>(kBI * (lane & 15) + bi);
     }
 
     static __device__ __forceinline__ f32x4 mma(float b, float w, f32x4 acc)
     {
-        if constexpr (kQuad)
+        if constexpr (kVec) {
+            acc[0] = __builtin_fmaf(b, w, acc[0]);
+            return acc;
+        } else if constexpr (kQuad) {
             return __builtin_amdgcn_mfma_f32_4x4x1f32(b, w, acc, 0, 0, 0);
-        else
+        } else {
             return __builtin_amdgcn_mfma_f32_16x16x4f32(b, w, acc, 0, 0, 0);
+        }
     }
 };
 
-template <int kBI, bool kQuad, bool kSrc1Transposed>
+template <int kBI, int kMode, bool kSrc1Transposed>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Direct<kBI, kQuad>::kMinWaves)))
+__attribute__((amdgpu_waves_per_eu(Direct<kBI, kMode>::kMinWaves)))
 void out_prod_direct_kernel(FusedArgs a)
 {
-    using D = Direct<kBI, kQuad>;
+    using D = Direct<kBI, kMode>;
     __shared__ float lds_scb[256];
     __shared__ f32x2 lds_pair[256];                  // (entry of low nibble, high nibble)
     __shared__ float lds_red[kBI * 32 * 64];         // a wave's partial tile
@@ -774,7 +792,7 @@ void out_prod_direct_kernel(FusedArgs a)
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < D::kAccV; ++v)
                     lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane] = acc[bi][bj][v];
     };
     const auto add = [&]() {
@@ -783,7 +801,7 @@ void out_prod_direct_kernel(FusedArgs a)
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < D::kAccV; ++v)
                     acc[bi][bj][v] = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
     };
     if (wave == 2)
@@ -804,7 +822,7 @@ void out_prod_direct_kernel(FusedArgs a)
     if (wave != 0)
         return;
     float *out = a.part + int64_t{split} * a.m * a.n_cols;
-    if constexpr (kQuad) {
+    if constexpr (D::kQuad || D::kVec) {
         // the lane groups of the four weight rows, (g0 + g1) + (g2 + g3), with
         // every lane of the wave still active for the exchanges
 #pragma unroll
@@ -812,7 +830,7 @@ void out_prod_direct_kernel(FusedArgs a)
 #pragma unroll
             for (int bj = 0; bj < 8; ++bj)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
+                for (int v = 0; v < D::kAccV; ++v) {
                     float x = acc[bi][bj][v] + lds_red[((bi * 8 + bj) * 4 + v) * 64 + lane];
                     x = x + __shfl_xor(x, 16);
                     acc[bi][bj][v] = x + __shfl_xor(x, 32);
@@ -822,7 +840,7 @@ void out_prod_direct_kernel(FusedArgs a)
 #pragma unroll
         for (int bi = 0; bi < kBI; ++bi)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
+            for (int v = 0; v < D::kAccV; ++v) {
                 const int64_t i = i0 + 4 * bi + v;  // the accumulator's row v of set bi
                 if (i >= a.m)
                     continue;
@@ -892,7 +910,7 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch (see plan_for).  `variant` (0..27) indexes the
+// The kernel for a launch (see plan_for).  `variant` (0..29) indexes the
 // kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
@@ -919,27 +937,29 @@ double tile_cost(int64_t m, int64_t tile_i)
     return static_cast<double>(ceil_div(m, tile_i) * tile_i) * rel;
 }
 
-template <int kBI, bool kQuad = false>
+template <int kBI, int kMode = 0>
 const void *direct_kernel(bool transposed)
 {
     return transposed
-               ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kQuad, true>)
-               : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kQuad, false>);
+               ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, true>)
+               : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, false>);
 }
 
 // The kernel for m dst rows.  The aligned path takes the direct kernel's
-// tiles: the 4-row sets for m <= 8, then 16, 32, 48 or 64 rows (m > 64
-// repeats the 64-row tile over the rows; the call splits such m into whole
-// 64-row tiles and a smaller rest, see row_ranges).  The byte path takes the
-// staged kernel.
+// tiles: the vector-unit row for m == 1, the 4-row sets for m <= 8, then 16,
+// 32, 48 or 64 rows (m > 64 repeats the 64-row tile over the rows; the call
+// splits such m into whole 64-row tiles and a smaller rest, see row_ranges).
+// The byte path takes the staged kernel.
 Plan plan_for(int64_t m, bool transposed, bool aligned8)
 {
     const int t = transposed ? 1 : 0;
     if (aligned8) {
+        if (m == 1)
+            return {direct_kernel<1, 2>(transposed), 1, 28 + t, true};
         if (m <= 4)
-            return {direct_kernel<1, true>(transposed), 4, 24 + t, true};
+            return {direct_kernel<1, 1>(transposed), 4, 24 + t, true};
         if (m <= 8)
-            return {direct_kernel<2, true>(transposed), 8, 26 + t, true};
+            return {direct_kernel<2, 1>(transposed), 8, 26 + t, true};
         if (m <= 16)
             return {direct_kernel<1>(transposed), 16, 16 + t, true};
         if (m <= 32)
@@ -961,7 +981,7 @@ Plan plan_for(int64_t m, bool transposed, bool aligned8)
     return {staged_kernel<64>(transposed), 64, 4 + 2 * t, false};
 }
 
-constexpr int kVariants = 28;
+constexpr int kVariants = 30;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 

@@ -98,7 +98,7 @@ def test_in_kernel_decode_is_bit_exact(layout, transposed, m):
 
 
 @pytest.mark.parametrize("transposed", [False, True])
-@pytest.mark.parametrize("m", [3, 5, 16, 70, 150])
+@pytest.mark.parametrize("m", [1, 3, 5, 16, 70, 150])
 def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
     """The direct kernel's full steps load without bounds checks: lanes past
     n_cols or past m read in-range elements whose products only reach dst
@@ -106,8 +106,8 @@ def test_src1_padding_and_ragged_edges_are_never_read(m, transposed):
     n_rows when transposed) holds NaN, the weight's last 128-column tile is
     ragged and its last 4-row step partial; a NaN that reached a stored
     element's sum would show, so dst row i must equal the oracle's weight row
-    sel[i] (the 4- and 8-row sets, the 16-row tile, and 64-row tiles with a
-    smaller tile for the rest)."""
+    sel[i] (the vector-unit row, the 4- and 8-row sets, the 16-row tile, and
+    64-row tiles with a smaller tile for the rest)."""
     n_rows, n_cols = 16 * 37 + 5, 400
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=777, n_rows=n_rows,
                            n_cols=n_cols)
@@ -218,10 +218,10 @@ def test_split_past_2_pow_32_weight_elements_keeps_the_checked_loads():
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
 def test_direct_tiles_steps_and_splits(n_rows, transposed):
-    """m <= 64 on the aligned path takes the direct kernel (4 or 8 dst rows
-    per tile on the 4 x 4 x 1 matrix instruction, whose lane groups are added
-    at the end; 16, 32, 48 or 64 rows on the 16 x 16 x 4 one, permuted within
-    the tile): 4-row steps spread over the workgroup's 4 waves, its
+    """m <= 64 on the aligned path takes the direct kernel (one dst row summed
+    on the vector unit at m = 1; 4 or 8 dst rows per tile on the 4 x 4 x 1
+    matrix instruction, whose lane groups are added at the end; 16, 32, 48 or
+    64 rows on the 16 x 16 x 4 one, permuted within the tile): 4-row steps spread over the workgroup's 4 waves, its
     full steps pipelined, the split's last partial step checked, and the
     waves' partial tiles added at the end.  Row counts below, at and just
     past a step and a wave round, a ragged last 128-column tile, and m at and
@@ -274,7 +274,7 @@ def test_row_ranges_keep_checked_loads_past_32_bit_offsets():
 
 
 @pytest.mark.parametrize("transposed", [False, True])
-@pytest.mark.parametrize("m", [3, 12, 16, 48, 100])
+@pytest.mark.parametrize("m", [1, 3, 12, 16, 48, 100])
 def test_infinite_src1_reaches_only_its_own_products(m, transposed):
     """An infinity in src1 must reach exactly the dst elements the sum gives
     it: each workgroup reads only the rows of its own split, and zeroes both
@@ -282,7 +282,7 @@ def test_infinite_src1_reaches_only_its_own_products(m, transposed):
     elsewhere.  One +inf per src1 column at a random row (the rows cover many
     splits); the NaN and infinity pattern of dst, and the infinities' signs,
     equal those of inf * W[r][j] added to the finite part, and every other
-    element is finite (direct tiles at m = 3, 12, 16 and 48; at m = 100 a
+    element is finite (direct tiles at m = 1, 3, 12, 16 and 48; at m = 100 a
     64-row tile and a 48-row tile for the other 36 rows)."""
     n_rows, n_cols = 4099, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=780 + m, n_rows=n_rows,
@@ -349,11 +349,11 @@ def test_selection_600000_rows_at_256_columns_is_bit_exact(m, transposed):
                                           f"workspace={'preferred' if ws is None else 'none'}")
 
 
-@pytest.mark.parametrize("m", [4, 8, 16, 32, 48, 64, 100, 512])
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 32, 48, 64, 100, 512])
 def test_selection_output_head_is_bit_exact(m):
     """Selection-matrix src1 over the 151 936 x 5 376 output head, both
-    orientations, at each tile of the direct kernel (4, 8, 16, 32, 48 and 64
-    rows), at m = 100 (a 64-row tile, then a 48-row tile for the other 36
+    orientations, at each tile of the direct kernel (the vector-unit row at
+    m = 1; 4, 8, 16, 32, 48 and 64 rows), at m = 100 (a 64-row tile, then a 48-row tile for the other 36
     rows) and at m = 512 (eight 64-row tiles): every row split is selected;
     dst equals the weight rows exactly."""
     wl = inputs.OUTPUT_HEAD
@@ -369,10 +369,11 @@ def test_selection_output_head_is_bit_exact(m):
                               f"fused output head m={m} transposed={transposed}")
 
 
-@pytest.mark.parametrize("m", [4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16])
 def test_output_head_both_orientations_and_against_the_blocked_route(m):
-    """The 151936 x 5376 output head with random src1 at m = 4 (the 4-row
-    set, whose lane groups add up at the end) and m = 16, both orientations,
+    """The 151936 x 5376 output head with random src1 at m = 1 (the vector
+    unit's fused multiply-adds), m = 4 (the 4-row set, whose lane groups add
+    up at the end) and m = 16, both orientations,
     within the summation bound; the fused and the row-blocked results agree
     within twice the bound."""
     case = dict(cases.OUTPUT_HEAD, m=m)
@@ -449,13 +450,14 @@ def test_edge_cases():
                                                                 device="cuda"))
 
 
-@pytest.mark.parametrize("m", [4, 32])
+@pytest.mark.parametrize("m", [1, 4, 32])
 def test_graph_capture_replays_with_splits(m):
     """The fused route -- kernel plus the reduction over row splits -- captured
     in a HIP graph and replayed several times, with new src1 values written
     eagerly between replays: every replay equals an eager call on the same
     src1 bit for bit (the result is deterministic for a given workspace).
-    m = 4 takes the 4-row set, m = 32 the 32-row tile."""
+    m = 1 takes the vector-unit row, m = 4 the 4-row set, m = 32 the 32-row
+    tile."""
     n_rows, n_cols = 20000, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=20000, n_rows=n_rows,
                            n_cols=n_cols)
