@@ -355,6 +355,33 @@ def test_beyond_2_pow_31_elements():
     torch.cuda.empty_cache()
 
 
+def test_row_windows_past_2_pow_31_and_2_pow_32_elements():
+    """64-bit indexing of the row-window call: a weight of 2^32 + 2^20
+    elements (2 GiB packed, n_cols = 4096), windows straddling elements
+    2^31 and 2^32, the weight's last rows, and a short window past 2^32
+    that starts inside a nested group (rows 2^20 + 7 .. + 2; a group of 256
+    blocks of 64 is 4 rows here), in FP16 and FP32; each equals the oracle's
+    elements."""
+    n_rows, n_cols = (1 << 20) + 256, 4096
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.02, seed=782, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    windows = [((1 << 19) - 150, 300),        # across element 2^31
+               ((1 << 20) - 150, 300),        # across element 2^32
+               (n_rows - 257, 257),           # the last rows
+               ((1 << 20) + 7, 3)]            # a short window past 2^32
+    for dt in ("f16", "f32"):
+        for r0, rows in windows:
+            say(f"window {dt} r0={r0} rows={rows}")
+            y = dq4.dq4_nested_dequant_rows(**dev, offset=float(x.offset), n_rows=n_rows,
+                                            n_cols=n_cols, r0=r0, rows=rows, blocksize=64,
+                                            out_dtype=torch_dtype(dt))
+            want = oracle_bits(x, dt, first=r0 * n_cols, count=rows * n_cols)
+            assert_bits_equal(bits_of(y), want, f"window {dt} r0={r0} rows={rows}")
+    del dev
+    torch.cuda.empty_cache()
+
+
 def test_bad_arguments_raise_and_write_nothing():
     x = inputs.make_inputs(1000, 64, "nf4", 0.03, seed=1)
     dev = dq4.to_device(x)
