@@ -1008,12 +1008,13 @@ int resident_per_cu(const Plan &plan, int device)
 }
 
 // The split of the rows.  Workgroups all do the same work, so the kernel
-// takes ceil(groups / resident) rounds of resident workgroups; the split
-// count is the smallest that brings the fraction of occupied slots,
+// takes ceil(groups / resident) rounds of resident workgroups; the preferred
+// split count is the smallest that brings the fraction of occupied slots,
 // groups / (rounds * resident), within 2 % of the best reachable with at most
-// kMaxSplits splits, at least kMinRowsPerSplit rows per split, and no more
-// partial tiles than max_partials (the workspace's capacity).  Returns the
-// rows per split.
+// kMaxSplits splits and at least kMinRowsPerSplit rows per split.  The call
+// takes the largest count up to that one whose partial tiles the workspace
+// holds (max_partials), so a workspace of the preferred size gives the
+// preferred split.  Returns the rows per split.
 int64_t rows_per_split(int64_t n_rows, int64_t tiles, int64_t resident, int64_t max_partials)
 {
     const auto occupied = [&](int64_t splits) {
@@ -1021,14 +1022,14 @@ int64_t rows_per_split(int64_t n_rows, int64_t tiles, int64_t resident, int64_t 
         return static_cast<double>(groups) /
                static_cast<double>(ceil_div(groups, resident) * resident);
     };
-    int64_t s_max = min(ceil_div(n_rows, kMinRowsPerSplit), max_partials);
-    s_max = min(s_max, kMaxSplits);
+    const int64_t s_max = min(ceil_div(n_rows, kMinRowsPerSplit), kMaxSplits);
     double best = occupied(1);
     for (int64_t s = 2; s <= s_max; ++s)
         best = std::max(best, occupied(s));
     int64_t splits = 1;
     while (splits < s_max && occupied(splits) < 0.98 * best)
         ++splits;
+    splits = max(int64_t{1}, min(splits, max_partials));
     return ceil_div(ceil_div(n_rows, splits), kStage) * kStage;
 }
 

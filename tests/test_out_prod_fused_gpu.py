@@ -393,6 +393,35 @@ def test_output_head_both_orientations_and_against_the_blocked_route(m):
                         "fused vs blocked", factor=2.0)
 
 
+@pytest.mark.parametrize("m", [1, 16, 100, 300])
+def test_preferred_workspace_is_enough_for_every_row_range(m):
+    """dq4_out_prod_fused_workspace_bytes sizes the workspace for the preferred
+    split of every row range of the call (m = 100 and 300 run two ranges that
+    reuse it): with exactly that many bytes the call takes the same splits,
+    and so gives the same bits, as with four times as many; with one byte
+    less it still runs, with fewer splits, within the summation bound."""
+    n_rows, n_cols = 6000, 384
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.01, seed=784, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(m))
+    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    exact, mag = out_prod_reference(x, n_rows, n_cols, b)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    assert preferred > 0 and preferred % 4 == 0
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64,
+              src1=_src1(b, False))
+    y_pref = dq4.dq4_out_prod_fused(**dev, **kw, workspace=torch.empty(
+        preferred // 4, device="cuda")).cpu().numpy()
+    y_big = dq4.dq4_out_prod_fused(**dev, **kw, workspace=torch.empty(
+        preferred, device="cuda")).cpu().numpy()
+    assert np.array_equal(y_pref.view(np.uint32), y_big.view(np.uint32))
+    check_sum_bound(y_pref, exact, mag, n_rows, f"m={m} preferred workspace")
+    y_less = dq4.dq4_out_prod_fused(**dev, **kw, workspace=torch.empty(
+        preferred // 4 - 1, device="cuda")).cpu().numpy()
+    check_sum_bound(y_less, exact, mag, n_rows, f"m={m} workspace one float short")
+
+
 @pytest.mark.parametrize("n_cols", [200, 201])
 @pytest.mark.parametrize("m", [150, 300])
 def test_ragged_tiles_every_split_and_determinism(m, n_cols):
