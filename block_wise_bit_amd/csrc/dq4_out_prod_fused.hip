@@ -557,6 +557,43 @@ struct Direct {
     }
 };
 
+// The 4 x 4 transpose of x across the four 16-lane rows of a wave: lane row r
+// holds x = (M[r][0], .., M[r][3]) and gets out[t] = M[t][r].  Swapping rows
+// 2-3 of one register with rows 0-1 of another, then odd rows with even rows,
+// is the usual two-level block transpose.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void transpose_rows4(u32x4 x, float (&out)[4])
+{
+    // x holds the loaded bits as integers: a bit_cast of a single element of
+    // a float vector read element 0 for every element with this compiler
+    uint32_t v0 = x[0], v1 = x[1], v2 = x[2], v3 = x[3];
+    auto p = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+    v0 = p[0];
+    v2 = p[1];
+    p = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+    v1 = p[0];
+    v3 = p[1];
+    p = __builtin_amdgcn_permlane16_swap(v0, v1, false, false);
+    v0 = p[0];
+    v1 = p[1];
+    p = __builtin_amdgcn_permlane16_swap(v2, v3, false, false);
+    v2 = p[0];
+    v3 = p[1];
+    out[0] = __builtin_bit_cast(float, v0);
+    out[1] = __builtin_bit_cast(float, v1);
+    out[2] = __builtin_bit_cast(float, v2);
+    out[3] = __builtin_bit_cast(float, v3);
+}
+
+template <int kBI>
+struct SuperLoad {
+    uint32_t packed4[4];
+    uint32_t code[4];
+    float absmax[4];
+    u32x4 b[kBI];  // src1 bits
+};
+
 template <int kBI, int kMode, bool kSrc1Transposed>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Direct<kBI, kMode>::kMinWaves)))
@@ -695,71 +732,148 @@ void out_prod_direct_kernel(FusedArgs a)
                 acc[bi][bj] = D::mma(use ? ld.b[bi] : 0.0f, use ? v[bj] : 0.0f, acc[bi][bj]);
     };
 
-    // Full steps: wave w takes steps w, w + 4, w + 8, ... below n_full.  Two
-    // banks of kDepth loads alternate: the steps of one bank are computed
-    // while the loads of the other fly.  (Written so that no loaded value is
-    // copied between registers -- a copy would wait for the load -- and so
-    // that the loop body updates the accumulators unconditionally: a
-    // conditional update keeps the old value live and made the compiler copy
-    // every accumulator on every step.)
-    // steps per register bank: at kBI >= 3 one step for a row-major src1
-    // (fewer registers, 3 % faster at m = 48 and 64), two for a transposed
-    // one, whose kBI loads per step are kBI separate rows (3 % slower with one)
-    constexpr int kDepth = kBI >= 3 ? (kSrc1Transposed ? 2 : 1) : 3;
-    constexpr int kBank = 4 * kDepth;  // steps of one bank
-    DirectLoad<kBI> bank0[kDepth], bank1[kDepth];
-    if (n_full > 0) {
-        // unconditional as in the loop (past n_full: step n_full - 1, unused),
-        // and issued in the loop's order: the counts of loads in flight that
-        // the loop waits for hold on entry too (left to reorder these loads,
-        // the compiler made the loop wait for all but a few of them)
+    // The full steps run in two banks of loads that alternate: the steps of
+    // one bank are computed while the loads of the other fly.  (Written so
+    // that no loaded value is copied between registers -- a copy would wait
+    // for the load -- and so that the loop body updates the accumulators
+    // unconditionally: a conditional update keeps the old value live and made
+    // the compiler copy every accumulator on every step.)
+    int first_tail = n_full;  // the checked steps start here
+    if constexpr (kSrc1Transposed && kMode == 0 && kBI <= 2) {
+        // A transposed src1 in the 16- and 32-row tiles: each of a step's
+        // src1 loads reads 16 separate rows of src1 (one line each).  Here a
+        // wave takes super-steps of 16 consecutive weight rows (4 steps; wave
+        // w takes super-steps w, w + 4, ..), lane row r loads rows
+        // 16 S + 4 r .. + 3 of its src1 column at once (16 bytes), and the
+        // wave's four lane rows swap them into place (transpose_rows4), so the
+        // src1 loads read 4 x fewer lines.  On the output head this made the
+        // 16- and 32-row tiles' time flat in m: m = 16 and 32 8 % faster, m =
+        // 28 4 %, and at most 2 % slower for a sparse tile (m = 9), whose
+        // clamped columns already share lines.  The 4- and 8-row sets (4
+        // distinct src1 rows per load) and the 48- and 64-row tiles measured
+        // no better with it.
+        const int n_super = n_full >> 2;
+        first_tail = n_super << 2;
+        uint32_t bq_off[kBI];
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            bank0[d] = load_full(min(wave + 4 * d, n_full - 1));
+        for (int bi = 0; bi < kBI; ++bi) {
+            const uint32_t il = min(D::src1_row(lane, bi), i_last);
+            bq_off[bi] = 4u * (il * ld_src1 + 4u * static_cast<uint32_t>(row));
+        }
+        const auto load_super = [&](int S) {
+            SuperLoad<kBI> ld;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t d = static_cast<uint32_t>(4 * S + t) * step_elems;
+                ld.packed4[t] = __builtin_amdgcn_raw_buffer_load_b32(packed_b, w_byte, d >> 1, 0);
+                const uint32_t cb = (c_lane + d) >> lb;
+                ld.code[t] = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb, 0, 0);
+                ld.absmax[t] = load_f32(absmax_b, 4u * ((g0 + cb) >> kNestedLog2));
+            }
+            const uint32_t sb = static_cast<uint32_t>(S) * (16u * 4u);
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                ld.b[bi] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(src1_b, bq_off[bi], sb, 0));
+            return ld;
+        };
+        const auto super_step = [&](const SuperLoad<kBI> &ld, bool use) {
+            float av[kBI][4];
+#pragma unroll
+            for (int bi = 0; bi < kBI; ++bi)
+                transpose_rows4(ld.b[bi], av[bi]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float v[8];
+                decode8(ld.packed4[t],
+                        block_scale(lds_scb[ld.code[t]], ld.absmax[t], a.offset), lds_pair, v);
+#pragma unroll
+                for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+                    for (int bi = 0; bi < kBI; ++bi)
+                        acc[bi][bj] = D::mma(use ? av[bi][t] : 0.0f, use ? v[bj] : 0.0f,
+                                             acc[bi][bj]);
+            }
+        };
+        SuperLoad<kBI> sl0, sl1;
+        if (n_super > 0) {
+            sl0 = load_super(min(wave, n_super - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            sl1 = load_super(min(wave + 4, n_super - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            bank1[d] = load_full(min(wave + kBank + 4 * d, n_full - 1));
+        int S0 = wave;  // the super-step in sl0
+        for (; S0 + 4 < n_super; S0 += 8) {
+            super_step(sl0, true);
+            sl0 = load_super(min(S0 + 8, n_super - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            super_step(sl1, true);
+            sl1 = load_super(min(S0 + 12, n_super - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    int s0 = wave;  // first step of bank0
-    for (; s0 + kBank + 4 * (kDepth - 1) < n_full; s0 += 2 * kBank) {
-        // Every step of both banks is below n_full.  The next loads are
-        // issued unconditionally (a step past n_full reloads step n_full - 1,
-        // unused): conditional loads would make the compiler's count of loads
-        // in flight inexact, and it then waits for all of them.  The
-        // scheduling barriers keep each step's loads right after its use of
-        // the registers they refill; left alone, the scheduler sank all of
-        // them to the end of the loop body, where the next iteration waited
-        // for them at once.
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            full_step(bank0[d]);
-            bank0[d] = load_full(min(s0 + 2 * kBank + 4 * d, n_full - 1));
-            __builtin_amdgcn_sched_barrier(0);
+        if (n_super > 0)
+            super_step(sl0, S0 < n_super);  // at most one left, in sl0
+    } else {
+        // wave w takes steps w, w + 4, w + 8, ... below n_full, kDepth steps
+        // per bank: at kBI >= 3 one for a row-major src1 (fewer registers, 3 %
+        // faster at m = 48 and 64), two for a transposed one, whose kBI loads
+        // per step are kBI separate rows (3 % slower with one)
+        constexpr int kDepth = kBI >= 3 ? (kSrc1Transposed ? 2 : 1) : 3;
+        constexpr int kBank = 4 * kDepth;  // steps of one bank
+        DirectLoad<kBI> bank0[kDepth], bank1[kDepth];
+        if (n_full > 0) {
+            // unconditional as in the loop (past n_full: step n_full - 1, unused),
+            // and issued in the loop's order: the counts of loads in flight that
+            // the loop waits for hold on entry too (left to reorder these loads,
+            // the compiler made the loop wait for all but a few of them)
+    #pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                bank0[d] = load_full(min(wave + 4 * d, n_full - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    #pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                bank1[d] = load_full(min(wave + kBank + 4 * d, n_full - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            full_step(bank1[d]);
-            bank1[d] = load_full(min(s0 + 3 * kBank + 4 * d, n_full - 1));
-            __builtin_amdgcn_sched_barrier(0);
+        int s0 = wave;  // first step of bank0
+        for (; s0 + kBank + 4 * (kDepth - 1) < n_full; s0 += 2 * kBank) {
+            // Every step of both banks is below n_full.  The next loads are
+            // issued unconditionally (a step past n_full reloads step n_full - 1,
+            // unused): conditional loads would make the compiler's count of loads
+            // in flight inexact, and it then waits for all of them.  The
+            // scheduling barriers keep each step's loads right after its use of
+            // the registers they refill; left alone, the scheduler sank all of
+            // them to the end of the loop body, where the next iteration waited
+            // for them at once.
+    #pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                full_step(bank0[d]);
+                bank0[d] = load_full(min(s0 + 2 * kBank + 4 * d, n_full - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    #pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                full_step(bank1[d]);
+                bank1[d] = load_full(min(s0 + 3 * kBank + 4 * d, n_full - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-    }
-    // at most 2 * kDepth - 1 full steps are left, all loaded
-    if (n_full > 0) {
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-            masked_step(bank0[d], s0 + 4 * d < n_full);
-#pragma unroll
-        for (int d = 0; d < kDepth - 1; ++d)
-            masked_step(bank1[d], s0 + kBank + 4 * d < n_full);
+        // at most 2 * kDepth - 1 full steps are left, all loaded
+        if (n_full > 0) {
+    #pragma unroll
+            for (int d = 0; d < kDepth; ++d)
+                masked_step(bank0[d], s0 + 4 * d < n_full);
+    #pragma unroll
+            for (int d = 0; d < kDepth - 1; ++d)
+                masked_step(bank1[d], s0 + kBank + 4 * d < n_full);
+        }
     }
     // the rest (the split's last, partial step; every step when the host
     // could not allow the full ones): 64-bit indices, both operands of a row
     // past the split zeroed
-    for (int s = n_full + ((wave - n_full) & 3); s < n_steps; s += 4) {
+    for (int s = first_tail + ((wave - first_tail) & 3); s < n_steps; s += 4) {
         const int64_t r = k_begin + int64_t{kDirectK} * s + row;
         const bool valid = r < k_end;
         DirectLoad<kBI> ld{};
