@@ -20,8 +20,12 @@ Prints ONE JSON line (rank 0, one GPU):
   cpu_baseline = the CPU oracle on the same inputs, on the host's threads over
                disjoint element ranges (single_core inside: on one thread)
 Timing protocol after the bitsandbytes issue's evidence plan ("B300 evidence
-plan"): >= 20 warmups, 7 timed batches of inner launches, every batch sample
-reported with median, p10 and p90.  Whatever --warmup asks for, at least 20
+plan"): >= 20 warmups; the timed region is K launches between one pair of
+events; right after it the same K launches run again in 7 batches with an
+event pair each, and every batch sample is reported with median, p10 and p90
+(kernel_us.batches_after).  The batch events stay out of the timed region
+because an event recorded between two launches holds the second one back
+until its timestamp is written.  Whatever --warmup asks for, at least 20
 untimed launches and 0.1 s of them run before each timed region
 (warmup_launches in the JSON line counts them): the first milliseconds of a
 burst of launches run slower while the GPU's clocks settle.
@@ -158,6 +162,40 @@ def warm_up(step, asked: int, torch) -> int:
         torch.cuda.synchronize()
         if k >= want and time.perf_counter() - t0 >= WARMUP_MIN_SECONDS:
             return k
+
+
+def timed_region(step, K: int, stream, torch):
+    """K calls of step(k) between one pair of events on `stream`, with
+    torch.cuda.synchronize() and the wall clock on both sides; returns (device
+    microseconds per step from the events, wall seconds for the region)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(K):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e3 / K, wall
+
+
+def timed_batches(step, per, stream, torch, first: int = 0):
+    """Consecutive batches of per[i] calls of step(k), k counting on from
+    `first`, each between its own pair of events; returns microseconds per
+    call for every batch."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in per]
+    torch.cuda.synchronize()
+    k = first
+    for (e0, e1), m in zip(evs, per):
+        e0.record(stream)
+        for _ in range(m):
+            step(k)
+            k += 1
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 / m for (e0, e1), m in zip(evs, per)]
 
 
 def raw_dequant_steps(dq4, sets, offset, n, bs, out_code, stream):
@@ -1034,7 +1072,7 @@ def launch_trace(args, torch, dq4, inputs) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=700, help="timed steps (split into 7 batches)")
+    ap.add_argument("--steps", type=int, default=700, help="timed steps (then sampled again in 7 batches)")
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (>= 20; the default lets clocks settle)")
     ap.add_argument("--rotate", type=int, default=6,
@@ -1141,51 +1179,32 @@ def main() -> int:
     print(f"[bench] {warm} warmup steps done ({args.warmup} asked for)", file=sys.stderr,
           flush=True)
 
-    # timed region: K steps in `batches` batches, one event pair per batch on
-    # the launch stream, wall clock around the whole region
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nbatch)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    k = 0
-    for (e0, e1), m in zip(evs, per):
-        e0.record(stream)
-        for _ in range(m):
-            step(k)
-            k += 1
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    batch_us = [e0.elapsed_time(e1) * 1e3 / m for (e0, e1), m in zip(evs, per)]
-    kernel_us = sum(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs) / K
+    # timed region: K steps with one event pair around all of them on the
+    # launch stream, and the wall clock around the region.  (An event recorded
+    # between two launches holds the next launch back until the timestamp is
+    # written, so the per-batch events stay out of this region.)
+    kernel_us, wall = timed_region(step, K, stream, torch)
     ms_per_step = wall * 1e3 / K
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
     print(f"[bench] {K} timed steps: {ms_per_step * 1e3:.2f} us/step wall, "
           f"{kernel_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
-
-    # the memory twin, after the timed region (whose last output is kept for
-    # the parity check first): the same tiles, loads and stores with no
-    # arithmetic, on the same buffer sets -- the ceiling of this access
-    # pattern on this GPU
     last_out = sets[(K - 1) % len(sets)][1].cpu()
+
+    # the spread: the same K steps again, right after the timed region, in
+    # `batches` batches with an event pair each
+    batch_us = timed_batches(step, per, stream, torch, first=K)
+
+    # the memory twin, timed the same way on the same buffer sets: the same
+    # tiles, loads and stores with no arithmetic -- the ceiling of this access
+    # pattern on this GPU
     twin_bytes = (n + 1) // 2 + 2 * n
 
     for dev, out in sets:
         dq4.dq4_memory_twin_f16(dev["packed"], n, out=out, stream=stream)
     twin = raw_twin_steps(dq4, sets, n, stream)
     warm_up(twin, args.warmup, torch)
-    tevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(nbatch)]
-    k = 0
-    for (e0, e1), m in zip(tevs, per):
-        e0.record(stream)
-        for _ in range(m):
-            twin(k)
-            k += 1
-        e1.record(stream)
-    torch.cuda.synchronize()
-    twin_us = sum(e0.elapsed_time(e1) * 1e3 for e0, e1 in tevs) / K
+    twin_us, _ = timed_region(twin, K, stream, torch)
     print(f"[bench] memory twin: {twin_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
 
     traffic = measured_traffic()
@@ -1211,7 +1230,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "elements_per_s": round(n / (kernel_us * 1e-6), 1),
-        "kernel_us": {"mean": round(kernel_us, 3), "batches": [round(b, 3) for b in batch_us],
+        "kernel_us": {"mean": round(kernel_us, 3),
+                      "batches_after": [round(b, 3) for b in batch_us],
                       "median": round(percentile(batch_us, 0.5), 3),
                       "p10": round(percentile(batch_us, 0.1), 3),
                       "p90": round(percentile(batch_us, 0.9), 3)},
