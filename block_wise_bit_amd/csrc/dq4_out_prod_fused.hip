@@ -1306,8 +1306,9 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
             dq4::rows_per_split(n_rows, tiles_i * tiles_j, resident, max_partials);
         const int64_t splits = dq4::ceil_div(n_rows, rps);
         const int64_t groups = splits * tiles_i * tiles_j;
-        if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kStage) > 0x7FFFFFFF)
-            return DQ4_EUNSUPPORTED;  // the kernel counts a split's stages in 32 bits
+        // the kernels count a split's stages (16 rows) or steps (4 rows) in 32 bits
+        if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kDirectK) > 0x7FFFFFFF)
+            return DQ4_EUNSUPPORTED;
         const bool full = plan.direct && dq4::direct_split_fits(rps, n_cols, ld_src1,
                                                                  plan.tile_i, transposed);
         float *r_dst = dst + r.i_begin * n_cols;

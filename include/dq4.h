@@ -284,7 +284,7 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
  * synchronized.  Errors: DQ4_EINVAL for bad sizes, a leading dimension that
  * is too small, a null pointer, or workspace_bytes > 0 with a null
  * workspace; DQ4_EUNSUPPORTED for a tile grid of more than 2^31 - 1
- * workgroups or a split of more than 16 * (2^31 - 1) rows; layout errors as
+ * workgroups or a split of more than 4 * (2^31 - 1) rows; layout errors as
  * for dq4_nested_dequant.
  */
 dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_codes,

@@ -215,6 +215,35 @@ def test_split_past_2_pow_32_weight_elements_keeps_the_checked_loads():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("m", [1, 4, 16, 64])
+def test_split_of_2_pow_31_steps_is_refused_before_any_launch(m):
+    """The kernels count a split's 4-row steps in 32 bits.  With no workspace
+    (one split) a weight of 2^33 + 16 rows would be 2^31 + 4 steps, so the
+    call must return DQ4_EUNSUPPORTED before it enqueues anything.  The rows
+    are only described: one small buffer stands in for every input, which
+    is why the check must come before any launch (a library built before
+    the check existed would launch here, so the test runs only on a library
+    newer than its source)."""
+    import ctypes
+    import os
+    src = os.path.join(os.path.dirname(dq4.__file__), "csrc", "dq4_out_prod_fused.hip")
+    if os.path.getmtime(dq4.LIBRARY_PATH) < os.path.getmtime(src):
+        pytest.skip("library older than its source")
+    lib = dq4.library()
+    n_rows, n_cols = (1 << 33) + 16, 8
+    small = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    dst = torch.full((m, n_cols), 7.0, dtype=torch.float32, device="cuda")
+    p = small.data_ptr()
+    stream = torch.cuda.current_stream().cuda_stream
+    for transposed in (0, 1):
+        ld = n_rows if transposed else m
+        st = lib.dq4_out_prod_fused(p, p, p, p, p, 0.0, n_rows, n_cols, 64, 256, p, m, ld,
+                                    transposed, dst.data_ptr(), None, 0, stream)
+        assert st == dq4.DQ4_EUNSUPPORTED, dq4.dq4_status_string(st)
+    torch.cuda.synchronize()
+    assert (dst.cpu() == 7.0).all()
+
+
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
 def test_direct_tiles_steps_and_splits(n_rows, transposed):
