@@ -594,7 +594,7 @@ struct SuperLoad {
     u32x4 b[kBI];  // src1 bits
 };
 
-template <int kBI, int kMode, bool kSrc1Transposed>
+template <int kBI, int kMode, bool kSrc1Transposed, bool kWholeBlocks>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Direct<kBI, kMode>::kMinWaves)))
 void out_prod_direct_kernel(FusedArgs a)
@@ -686,13 +686,31 @@ void out_prod_direct_kernel(FusedArgs a)
     const uint32_t w_byte = w_elem >> 1, c_lane = bl0 + w_elem;
     const uint32_t step_elems = kDirectK * n_cols;
     const uint32_t step_b = kSrc1Transposed ? 4u * kDirectK : 4u * kDirectK * ld_src1;
+    // When a step spans whole blocks (kWholeBlocks: kDirectK * n_cols is a
+    // multiple of the block size), the lane's block at step s is its block at
+    // step 0 plus s times the step's block count: the code's offset is then a
+    // lane constant plus a uniform part, and only the absmax index needs
+    // vector instructions (3 instead of 5 a step).
+    const uint32_t cb_lane = c_lane >> lb, ga_lane = g0 + cb_lane;
+    const uint32_t step_blocks = step_elems >> lb;
+    // the code and absmax of the lane's block at the step starting d elements
+    // past the split's first row (d = s * step_elems)
+    const auto load_meta = [&](uint32_t s, uint32_t d, uint32_t &code, float &absmax) {
+        if constexpr (kWholeBlocks) {
+            const uint32_t sblk = s * step_blocks;
+            code = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb_lane, sblk, 0);
+            absmax = load_f32(absmax_b, 4u * ((ga_lane + sblk) >> kNestedLog2));
+        } else {
+            const uint32_t cb = (c_lane + d) >> lb;  // the lane's block, from bh0
+            code = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb, 0, 0);
+            absmax = load_f32(absmax_b, 4u * ((g0 + cb) >> kNestedLog2));
+        }
+    };
     const auto load_full = [&](int s) {
         DirectLoad<kBI> ld;
         const uint32_t d = static_cast<uint32_t>(s) * step_elems;  // the step's first element
         ld.packed4 = __builtin_amdgcn_raw_buffer_load_b32(packed_b, w_byte, d >> 1, 0);
-        const uint32_t cb = (c_lane + d) >> lb;  // the lane's block, from bh0
-        ld.code = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb, 0, 0);
-        ld.absmax = load_f32(absmax_b, 4u * ((g0 + cb) >> kNestedLog2));
+        load_meta(static_cast<uint32_t>(s), d, ld.code, ld.absmax);
         const uint32_t sb = static_cast<uint32_t>(s) * step_b;
 #pragma unroll
         for (int bi = 0; bi < kBI; ++bi)
@@ -766,9 +784,7 @@ void out_prod_direct_kernel(FusedArgs a)
             for (int t = 0; t < 4; ++t) {
                 const uint32_t d = static_cast<uint32_t>(4 * S + t) * step_elems;
                 ld.packed4[t] = __builtin_amdgcn_raw_buffer_load_b32(packed_b, w_byte, d >> 1, 0);
-                const uint32_t cb = (c_lane + d) >> lb;
-                ld.code[t] = __builtin_amdgcn_raw_buffer_load_b8(code_b, cb, 0, 0);
-                ld.absmax[t] = load_f32(absmax_b, 4u * ((g0 + cb) >> kNestedLog2));
+                load_meta(static_cast<uint32_t>(4 * S + t), d, ld.code[t], ld.absmax[t]);
             }
             const uint32_t sb = static_cast<uint32_t>(S) * (16u * 4u);
 #pragma unroll
@@ -1024,7 +1040,7 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
-// The kernel for a launch (see plan_for).  `variant` (0..29) indexes the
+// The kernel for a launch (see plan_for).  `variant` (0..43) indexes the
 // kernel for the occupancy cache.
 struct Plan {
     const void *kernel;
@@ -1052,50 +1068,56 @@ double tile_cost(int64_t m, int64_t tile_i)
 }
 
 template <int kBI, int kMode = 0>
-const void *direct_kernel(bool transposed)
+const void *direct_kernel(bool transposed, bool whole)
 {
+    if (whole)
+        return transposed
+                   ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, true, true>)
+                   : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, false, true>);
     return transposed
-               ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, true>)
-               : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, false>);
+               ? reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, true, false>)
+               : reinterpret_cast<const void *>(&out_prod_direct_kernel<kBI, kMode, false, false>);
 }
 
 // The kernel for m dst rows.  The aligned path takes the direct kernel's
 // tiles: the vector-unit row for m == 1, the 4-row sets for m <= 8, then 16,
 // 32, 48 or 64 rows (m > 64 repeats the 64-row tile over the rows; the call
 // splits such m into whole 64-row tiles and a smaller rest, see row_ranges).
-// The byte path takes the staged kernel.
-Plan plan_for(int64_t m, bool transposed, bool aligned8)
+// The byte path takes the staged kernel.  `whole`: a direct step of 4 weight
+// rows spans whole blocks (4 * n_cols is a multiple of the block size).
+Plan plan_for(int64_t m, bool transposed, bool aligned8, bool whole)
 {
-    const int t = transposed ? 1 : 0;
+    const int t = (transposed ? 1 : 0) + (whole ? 14 : 0);
     if (aligned8) {
         if (m == 1)
-            return {direct_kernel<1, 2>(transposed), 1, 28 + t, true};
+            return {direct_kernel<1, 2>(transposed, whole), 1, 28 + t, true};
         if (m <= 4)
-            return {direct_kernel<1, 1>(transposed), 4, 24 + t, true};
+            return {direct_kernel<1, 1>(transposed, whole), 4, 24 + t, true};
         if (m <= 8)
-            return {direct_kernel<2, 1>(transposed), 8, 26 + t, true};
+            return {direct_kernel<2, 1>(transposed, whole), 8, 26 + t, true};
         if (m <= 16)
-            return {direct_kernel<1>(transposed), 16, 16 + t, true};
+            return {direct_kernel<1>(transposed, whole), 16, 16 + t, true};
         if (m <= 32)
-            return {direct_kernel<2>(transposed), 32, 18 + t, true};
+            return {direct_kernel<2>(transposed, whole), 32, 18 + t, true};
         if (m <= 48)
-            return {direct_kernel<3>(transposed), 48, 22 + t, true};
-        return {direct_kernel<4>(transposed), 64, 20 + t, true};
+            return {direct_kernel<3>(transposed, whole), 48, 22 + t, true};
+        return {direct_kernel<4>(transposed, whole), 64, 20 + t, true};
     }
+    const int ts = transposed ? 1 : 0;
     if (m <= 16)
-        return {staged_kernel<16>(transposed), 16, 2 * t, false};
+        return {staged_kernel<16>(transposed), 16, 2 * ts, false};
     int64_t best = 64;
     for (const int64_t w : {128, 256})
         if (tile_cost(m, w) < tile_cost(m, best))
             best = w;
     if (best == 256)
-        return {staged_kernel<256>(transposed), 256, 12 + 2 * t, false};
+        return {staged_kernel<256>(transposed), 256, 12 + 2 * ts, false};
     if (best == 128)
-        return {staged_kernel<128>(transposed), 128, 8 + 2 * t, false};
-    return {staged_kernel<64>(transposed), 64, 4 + 2 * t, false};
+        return {staged_kernel<128>(transposed), 128, 8 + 2 * ts, false};
+    return {staged_kernel<64>(transposed), 64, 4 + 2 * ts, false};
 }
 
-constexpr int kVariants = 30;
+constexpr int kVariants = 44;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][kVariants];
 
@@ -1177,17 +1199,17 @@ struct RowRange {
     Plan plan;
 };
 
-int row_ranges(int64_t m, bool transposed, bool aligned8, RowRange (&r)[2])
+int row_ranges(int64_t m, bool transposed, bool aligned8, bool whole_blocks, RowRange (&r)[2])
 {
     if (aligned8 && m > 64) {
         const int64_t whole = m / 64 * 64;
-        r[0] = {0, whole, plan_for(64, transposed, true)};
+        r[0] = {0, whole, plan_for(64, transposed, true, whole_blocks)};
         if (whole == m)
             return 1;
-        r[1] = {whole, m - whole, plan_for(m - whole, transposed, true)};
+        r[1] = {whole, m - whole, plan_for(m - whole, transposed, true, whole_blocks)};
         return 2;
     }
-    r[0] = {0, m, plan_for(m, transposed, aligned8)};
+    r[0] = {0, m, plan_for(m, transposed, aligned8, whole_blocks)};
     return 1;
 }
 
@@ -1215,9 +1237,10 @@ int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64
     // the largest partials any variant of the kernels would write for this
     // shape (the row ranges of a call use the workspace one after the other)
     int64_t bytes = 0;
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < 8; ++v) {
         dq4::RowRange ranges[2];
-        const int n_ranges = dq4::row_ranges(m, (v & 1) != 0, (v & 2) != 0, ranges);
+        const int n_ranges =
+            dq4::row_ranges(m, (v & 1) != 0, (v & 2) != 0, (v & 4) != 0, ranges);
         for (int k = 0; k < n_ranges; ++k) {
             const dq4::RowRange &r = ranges[k];
             const int64_t tiles =
@@ -1256,8 +1279,11 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     const int64_t count = m * n_cols;
     const bool aligned8 = n_cols % 8 == 0 && reinterpret_cast<uintptr_t>(packed) % 4 == 0;
     const bool transposed = src1_transposed != 0;
+    // blocksize is a power of two >= 32, so 4 * n_cols is a multiple of it
+    // exactly when n_cols is a multiple of a quarter of it
+    const bool whole_blocks = n_cols % (blocksize / dq4::kDirectK) == 0;
     dq4::RowRange ranges[2];
-    const int n_ranges = dq4::row_ranges(m, transposed, aligned8, ranges);
+    const int n_ranges = dq4::row_ranges(m, transposed, aligned8, whole_blocks, ranges);
     const int64_t tiles_j = dq4::ceil_div(n_cols, dq4::kTileJ);
     if (n_rows > 0) {
         if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 || !src1)

@@ -47,7 +47,7 @@ def test_kernels_present(asm):
                           ("dq4_value_tile_kernel", 3), ("dq4_value_elem_kernel", 3),
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
                           ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
-                          ("out_prod_fused_kernel", 8), ("out_prod_direct_kernel", 14),
+                          ("out_prod_fused_kernel", 8), ("out_prod_direct_kernel", 28),
                           ("out_prod_reduce_kernel", 1),
                           ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1),
                           ("dq4_shift_tile_kernel", 23)):
