@@ -244,9 +244,10 @@ def test_split_of_2_pow_31_steps_is_refused_before_any_launch(m):
     assert (dst.cpu() == 7.0).all()
 
 
+@pytest.mark.parametrize("blocksize", [32, 64])
 @pytest.mark.parametrize("transposed", [False, True])
 @pytest.mark.parametrize("n_rows", [1, 3, 4, 5, 37, 1000, 4099])
-def test_direct_tiles_steps_and_splits(n_rows, transposed):
+def test_direct_tiles_steps_and_splits(n_rows, transposed, blocksize):
     """m <= 64 on the aligned path takes the direct kernel (one dst row summed
     on the vector unit at m = 1; 4 or 8 dst rows per tile on the 4 x 4 x 1
     matrix instruction, whose lane groups are added at the end; 16, 32, 48 or
@@ -255,9 +256,11 @@ def test_direct_tiles_steps_and_splits(n_rows, transposed):
     waves' partial tiles added at the end.  Row counts below, at and just
     past a step and a wave round, a ragged last 128-column tile, and m at and
     past each tile width and ragged within it (with and without row splits):
-    dst row i equals the oracle's weight row sel[i]."""
+    dst row i equals the oracle's weight row sel[i].  At 136 columns a step
+    of 4 rows spans whole blocks of 32 (the kernels' whole-block indexing)
+    but not of 64 (the general indexing)."""
     n_cols = 136
-    x = inputs.make_inputs(n_rows * n_cols, 32, "fp4", 0.07, seed=n_rows + 901,
+    x = inputs.make_inputs(n_rows * n_cols, blocksize, "fp4", 0.07, seed=n_rows + 901,
                            n_rows=n_rows, n_cols=n_cols)
     dev = dq4.to_device(x)
     w = oracle_bits(x, "f32").view(np.float32).reshape(n_rows, n_cols)
@@ -268,8 +271,9 @@ def test_direct_tiles_steps_and_splits(n_rows, transposed):
         b[sel, np.arange(m)] = 1.0
         for ws in (None, torch.empty(0, device="cuda")):
             y = dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=n_rows,
-                                       n_cols=n_cols, blocksize=32, src1=_src1(b, transposed),
-                                       src1_transposed=transposed, workspace=ws).cpu().numpy()
+                                       n_cols=n_cols, blocksize=blocksize,
+                                       src1=_src1(b, transposed), src1_transposed=transposed,
+                                       workspace=ws).cpu().numpy()
             bad = np.argwhere(y != w[sel])
             assert bad.size == 0, f"m={m}: first mismatch at (i, j) = {bad[0]}"
 
