@@ -538,7 +538,7 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
                "sample": f"rows 0..{rows_s - 1} of {wl.n_rows} (the first row window), m = {m}: "
                          f"the C oracle's dequantization on {host_threads()} threads "
                          f"({t_deq:.2f} s) then numpy's float64 product ({t_mm:.2f} s)"}
-        sampled = {"rows": rows_s, "max_error_over_fp32_bound": round(float(excess.max()), 4),
+        sampled = {"rows": rows_s, "max_error_over_fp32_bound": float(f"{float(excess.max()):.3g}"),
                    "within_bound": bool(excess.max() <= 1.0)}
         del a_s, w_s, ref, bound, got_s, dst_s
     print(json.dumps({
