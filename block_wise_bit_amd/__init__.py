@@ -22,7 +22,7 @@ cannot be loaded, every call raises.
                                                    (row-blocked out_prod, FP32 GEMM)
     dq4_out_prod_fused(..., n_rows, n_cols, blocksize, src1, ...) -> tensor
                                                    (out_prod, dequantization in the GEMM)
-    dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m) -> int
+    dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, src1_transposed=False) -> int
     dq4_dequant_linear(..., n_out, n_in, blocksize, x, op) -> tensor
                                                    (Y = X W^T or G W, FP16/BF16 GEMM)
     dq4_int8_prep(A, CB, SCB, cols) -> (subA, subB)  (LLM.int8 correction operands)
@@ -89,7 +89,7 @@ def library() -> ctypes.CDLL:
     lib.dq4_out_prod_rows.restype = i32
     lib.dq4_out_prod_fused.argtypes = lib.dq4_out_prod_rows.argtypes
     lib.dq4_out_prod_fused.restype = i32
-    lib.dq4_out_prod_fused_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dq4_out_prod_fused_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.dq4_out_prod_fused_workspace_bytes.restype = i64
     lib.dq4_dequant_linear.argtypes = [P, P, P, P, P, f32, i64, i64, i32, i32, i32, i32, P, i64,
                                        P, P, P]
@@ -444,13 +444,16 @@ def dq4_out_prod_rows(packed, scale_codes, nested_absmax, scale_codebook, codebo
     return dst
 
 
-def dq4_out_prod_fused_workspace_bytes(n_rows: int, n_cols: int, m: int, device=None) -> int:
+def dq4_out_prod_fused_workspace_bytes(n_rows: int, n_cols: int, m: int, device=None,
+                                       src1_transposed: bool = False) -> int:
     """Workspace bytes for dq4_out_prod_fused's preferred row split on
-    `device` (default: the current device); 0 when it prefers one split."""
+    `device` (default: the current device) with a src1 of this orientation
+    (for a transposed one, with its row-major copy); 0 when it prefers one
+    split."""
     torch = _torch()
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        return int(library().dq4_out_prod_fused_workspace_bytes(int(n_rows), int(n_cols),
-                                                                int(m)))
+        return int(library().dq4_out_prod_fused_workspace_bytes(
+            int(n_rows), int(n_cols), int(m), 1 if src1_transposed else 0))
 
 
 def dq4_out_prod_fused(packed, scale_codes, nested_absmax, scale_codebook, codebook4,
@@ -459,15 +462,18 @@ def dq4_out_prod_fused(packed, scale_codes, nested_absmax, scale_codebook, codeb
                        nested_blocksize: int = NESTED_BLOCKSIZE, stream=None):
     """The same sum as dq4_out_prod_rows, with the 4-bit weight decoded inside
     an FP32 matrix-core GEMM (no dequantized copy in HBM).  `workspace`
-    (FP32, for partial sums over row splits) is allocated at the preferred
-    size when None; an empty tensor means one split.  Returns dst."""
+    (FP32, for partial sums over row splits and, for a transposed src1, its
+    row-major copy) is allocated at the preferred size for src1's
+    orientation when None; an empty tensor means one split and a transposed
+    src1 read in place.  Returns dst."""
     torch = _torch()
     n_rows, n_cols = int(n_rows), int(n_cols)
     device, m, ld, dst = _out_prod_operands(
         torch, packed, scale_codes, nested_absmax, scale_codebook, codebook4, n_rows, n_cols,
         blocksize, nested_blocksize, src1, src1_transposed, dst, stream)
     if workspace is None:
-        nbytes = dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, device)
+        nbytes = dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, device,
+                                                    src1_transposed=src1_transposed)
         workspace = _used_on(torch.empty(max(nbytes // 4, 0), dtype=torch.float32,
                                          device=device), stream)
     workspace = _f32_workspace(torch, workspace, device)

@@ -1035,6 +1035,41 @@ __global__ __launch_bounds__(kThreads) void out_prod_zero_kernel(float *dst, int
         dst[x] = 0.0f;
 }
 
+// A transposed src1 (m rows of n_rows floats, leading dimension ld) copied
+// into a row-major n_rows x m buffer: out[r * m + i] = src1[i * ld + r].  One
+// workgroup moves a 64 x 64 tile through LDS: it reads 64 consecutive floats
+// of each src1 row and writes each out row's run of the tile's columns (for
+// m <= 64 the tile's rows of out are one contiguous span).  Bit copies only.
+constexpr int kTrTile = 64;
+
+// The grid is (tiles of 64 rows r, tiles of 64 columns i).
+__global__ __launch_bounds__(kThreads) void src1_transpose_kernel(const float *src1, int64_t ld,
+                                                                  int64_t m, int64_t n_rows,
+                                                                  float *out)
+{
+    __shared__ float tile[kTrTile][kTrTile + 1];
+    const int t = threadIdx.x;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTrTile;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kTrTile;
+    const int nr = static_cast<int>(min(int64_t{kTrTile}, n_rows - r0));
+    const int ni = static_cast<int>(min(int64_t{kTrTile}, m - i0));
+    for (int k = t; k < kTrTile * kTrTile; k += kThreads) {
+        const int ii = k / kTrTile, rr = k % kTrTile;
+        if (ii < ni && rr < nr)
+            tile[ii][rr] = src1[(i0 + ii) * ld + r0 + rr];
+    }
+    __syncthreads();
+    // lanes step through the tile's rows in runs of the next power of two
+    // of ni (shifts, not a division: the compiler expands a 32-bit division
+    // into floating-point instructions)
+    const int lg = 32 - __clz(ni - 1);  // ni >= 1; ni == 1 gives 0
+    for (int k = t; k < (nr << lg); k += kThreads) {
+        const int rr = k >> lg, ii = k & ((1 << lg) - 1);
+        if (ii < ni)
+            out[(r0 + rr) * m + i0 + ii] = tile[ii][rr];
+    }
+}
+
 int64_t ceil_div(int64_t a, int64_t b)
 {
     return (a + b - 1) / b;
@@ -1213,6 +1248,78 @@ int row_ranges(int64_t m, bool transposed, bool aligned8, bool whole_blocks, Row
     return 1;
 }
 
+// Bytes of partial tiles the preferred row split of each of the ranges
+// writes (0 when each prefers one split); the ranges use the workspace one
+// after the other, so the largest counts.
+int64_t partial_bytes(const RowRange *r, int n_ranges, int64_t n_rows, int64_t n_cols,
+                      int device)
+{
+    int64_t bytes = 0;
+    for (int k = 0; k < n_ranges; ++k) {
+        const int64_t tiles = ceil_div(r[k].m, r[k].plan.tile_i) * ceil_div(n_cols, kTileJ);
+        const int64_t resident =
+            int64_t{compute_units(device)} * resident_per_cu(r[k].plan, device);
+        const int64_t rps = rows_per_split(n_rows, tiles, resident, kMaxSplits);
+        const int64_t splits = ceil_div(n_rows, rps);
+        if (splits > 1)
+            bytes = std::max(bytes, splits * r[k].m * n_cols * 4);
+    }
+    return bytes;
+}
+
+int64_t preferred_partial_bytes(int64_t n_rows, int64_t n_cols, int64_t m, bool transposed,
+                                bool aligned8, bool whole, int device)
+{
+    RowRange ranges[2];
+    const int n_ranges = row_ranges(m, transposed, aligned8, whole, ranges);
+    return partial_bytes(ranges, n_ranges, n_rows, n_cols, device);
+}
+
+// Bytes of a row-major copy of `cols` columns of a transposed src1 in the
+// workspace (rounded so that the partials after it stay 256-byte aligned).
+int64_t src1_copy_bytes(int64_t n_rows, int64_t cols)
+{
+    return (n_rows * cols * 4 + 255) / 256 * 256;
+}
+
+// A transposed src1 in the 48- and 64-row direct tiles reads 16 lines per
+// load where a row-major one reads 4, and a row-major copy of the range's
+// columns pays for itself once such a tile is at least 7/8 full.  Measured
+// on the output head against the in-place read: m = 44 .. 48 and 60 .. 64
+// 2-6 % faster with the copy, m = 52 and 56 within 1 %, m = 33 .. 40 (a
+// sparse 48-row tile, whose unused lanes share lines) 1-2 % slower; whole
+// 64-row ranges 2-6 % faster; and a 1-row rest range 0.4-0.6 % slower
+// reading a wide copy than reading src1 in place.  The narrower tiles (4-row
+// sets, and the 16- and 32-row tiles with their super-steps) were within
+// 1 % either way.
+bool copy_pays(const RowRange &r)
+{
+    return r.plan.direct && r.plan.tile_i >= 48 && r.m * 8 >= int64_t{r.plan.tile_i} * 7;
+}
+
+// For a transposed src1 on the aligned path: marks the ranges whose columns
+// go through the row-major copy, re-plans them row-major, and sets the
+// copied columns [*c0, *c1) (the copied ranges are adjacent).  Returns the
+// copy's bytes (0: nothing is copied).
+int64_t plan_copy(int64_t n_rows, int64_t m, bool whole, RowRange (&r)[2], int n_ranges,
+                  bool (&copied)[2], int64_t *c0, int64_t *c1)
+{
+    *c0 = *c1 = 0;
+    copied[0] = copied[1] = false;
+    if (m <= 1 || n_rows > INT64_MAX / 8 / m)
+        return 0;
+    for (int k = 0; k < n_ranges; ++k) {
+        if (!copy_pays(r[k]))
+            continue;
+        if (*c1 == *c0)
+            *c0 = r[k].i_begin;
+        *c1 = r[k].i_begin + r[k].m;
+        copied[k] = true;
+        r[k].plan = plan_for(r[k].m, false, true, whole);
+    }
+    return *c1 > *c0 ? src1_copy_bytes(n_rows, *c1 - *c0) : 0;
+}
+
 dq4_status_t grid_size(int64_t count, int device, uint32_t *grid)
 {
     int64_t g = ceil_div(count, kThreads);
@@ -1226,33 +1333,38 @@ dq4_status_t grid_size(int64_t count, int device, uint32_t *grid)
 
 extern "C" {
 
-int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m)
+int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m,
+                                           int32_t src1_transposed)
 {
     if (n_rows <= 0 || n_cols <= 0 || m <= 0 || n_cols > INT64_MAX / m ||
-        m * n_cols > INT64_MAX / 4 / dq4::kMaxSplits)
+        m * n_cols > INT64_MAX / 4 / dq4::kMaxSplits || n_rows > INT64_MAX / 8 / m ||
+        (src1_transposed != 0 && src1_transposed != 1))
         return 0;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess)
         return 0;
-    // the largest partials any variant of the kernels would write for this
-    // shape (the row ranges of a call use the workspace one after the other)
+    // a one-column src1 reads the same memory in either orientation
+    const bool transposed = src1_transposed != 0 && m > 1;
+    // the largest partials any kernel variant would write for this shape and
+    // orientation (packed alignment and block size are not known here)
     int64_t bytes = 0;
-    for (int v = 0; v < 8; ++v) {
-        dq4::RowRange ranges[2];
-        const int n_ranges =
-            dq4::row_ranges(m, (v & 1) != 0, (v & 2) != 0, (v & 4) != 0, ranges);
-        for (int k = 0; k < n_ranges; ++k) {
-            const dq4::RowRange &r = ranges[k];
-            const int64_t tiles =
-                dq4::ceil_div(r.m, r.plan.tile_i) * dq4::ceil_div(n_cols, dq4::kTileJ);
-            const int64_t resident =
-                int64_t{dq4::compute_units(device)} * dq4::resident_per_cu(r.plan, device);
-            const int64_t rps = dq4::rows_per_split(n_rows, tiles, resident, dq4::kMaxSplits);
-            const int64_t splits = dq4::ceil_div(n_rows, rps);
-            if (splits > 1)
-                bytes = std::max(bytes, splits * r.m * n_cols * 4);
+    for (int v = 0; v < 4; ++v)
+        bytes = std::max(bytes, dq4::preferred_partial_bytes(n_rows, n_cols, m, transposed,
+                                                             (v & 1) != 0, (v & 2) != 0, device));
+    // a transposed src1 on an aligned weight: the row-major copy of the
+    // columns whose tiles take it, and the partials of the plan that reads it
+    if (transposed && n_cols % 8 == 0)
+        for (int whole = 0; whole < 2; ++whole) {
+            dq4::RowRange ranges[2];
+            const int n_ranges = dq4::row_ranges(m, true, true, whole != 0, ranges);
+            bool copied[2];
+            int64_t c0 = 0, c1 = 0;
+            const int64_t copy =
+                dq4::plan_copy(n_rows, m, whole != 0, ranges, n_ranges, copied, &c0, &c1);
+            if (copy > 0)
+                bytes = std::max(bytes, copy + dq4::partial_bytes(ranges, n_ranges, n_rows,
+                                                                  n_cols, device));
         }
-    }
     return bytes;
 }
 
@@ -1278,12 +1390,12 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
         return DQ4_EINVAL;
     const int64_t count = m * n_cols;
     const bool aligned8 = n_cols % 8 == 0 && reinterpret_cast<uintptr_t>(packed) % 4 == 0;
-    const bool transposed = src1_transposed != 0;
+    bool transposed = src1_transposed != 0;
     // blocksize is a power of two >= 32, so 4 * n_cols is a multiple of it
     // exactly when n_cols is a multiple of a quarter of it
     const bool whole_blocks = n_cols % (blocksize / dq4::kDirectK) == 0;
     dq4::RowRange ranges[2];
-    const int n_ranges = dq4::row_ranges(m, transposed, aligned8, whole_blocks, ranges);
+    int n_ranges = dq4::row_ranges(m, transposed, aligned8, whole_blocks, ranges);
     const int64_t tiles_j = dq4::ceil_div(n_cols, dq4::kTileJ);
     if (n_rows > 0) {
         if (!packed || !scale_codes || !nested_absmax || !scale_codebook || !codebook4 || !src1)
@@ -1303,6 +1415,60 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
     if (e != hipSuccess)
         return dq4::hip_failed(e);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // each range's src1: where its values are, their leading dimension and
+    // orientation
+    const float *r_src[2];
+    int64_t r_ld[2];
+    bool r_tr[2];
+    for (int k = 0; k < n_ranges; ++k) {
+        r_tr[k] = transposed;
+        r_ld[k] = ld_src1;
+        r_src[k] = transposed ? src1 + ranges[k].i_begin * ld_src1 : src1 + ranges[k].i_begin;
+    }
+    if (n_rows > 0 && transposed && m == 1) {
+        // one src1 row: B[r][0] = src1[r], the row-major layout with ld 1
+        r_tr[0] = false;
+        r_ld[0] = 1;
+        r_src[0] = src1;
+        n_ranges = dq4::row_ranges(m, false, aligned8, whole_blocks, ranges);
+    } else if (n_rows > 0 && transposed && aligned8) {
+        // The ranges whose tiles read a transposed src1 badly (copy_pays) take
+        // a row-major copy of their columns when the workspace holds it and the
+        // partials of the plan that reads it: one more kernel writes the copy
+        // at the start of the workspace, and those ranges run as for a
+        // row-major src1 on it, with the rest of the workspace.
+        dq4::RowRange planned[2] = {ranges[0], ranges[1]};
+        bool copied[2];
+        int64_t c0 = 0, c1 = 0;
+        const int64_t copy_bytes = dq4::plan_copy(n_rows, m, whole_blocks, planned, n_ranges,
+                                                  copied, &c0, &c1);
+        const int64_t tiles_r = dq4::ceil_div(n_rows, dq4::kTrTile);
+        const int64_t tiles_c = dq4::ceil_div(c1 - c0, dq4::kTrTile);
+        if (copy_bytes > 0 && tiles_r <= 0x7FFFFFFF && tiles_c <= 65535 &&
+            workspace_bytes >= copy_bytes + dq4::partial_bytes(planned, n_ranges, n_rows,
+                                                               n_cols, device)) {
+            const float *in = src1 + c0 * ld_src1;
+            int64_t ld_in = ld_src1, cols = c1 - c0, nr = n_rows;
+            float *copy = workspace;
+            void *params[] = {&in, &ld_in, &cols, &nr, &copy};
+            e = hipLaunchKernel(reinterpret_cast<const void *>(&dq4::src1_transpose_kernel),
+                                dim3(static_cast<uint32_t>(tiles_r),
+                                     static_cast<uint32_t>(tiles_c)),
+                                dim3(dq4::kThreads), params, 0, s);
+            if (e != hipSuccess)
+                return dq4::hip_failed(e);
+            for (int k = 0; k < n_ranges; ++k) {
+                ranges[k] = planned[k];
+                if (copied[k]) {
+                    r_tr[k] = false;
+                    r_ld[k] = cols;
+                    r_src[k] = copy + (ranges[k].i_begin - c0);
+                }
+            }
+            workspace += copy_bytes / 4;
+            workspace_bytes -= copy_bytes;
+        }
+    }
     if (n_rows == 0) {  // an empty sum: dst = 0
         uint32_t grid = 0;
         dq4::grid_size(count, device, &grid);
@@ -1335,12 +1501,11 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
         // the kernels count a split's stages (16 rows) or steps (4 rows) in 32 bits
         if (groups > 0x7FFFFFFF || dq4::ceil_div(rps, dq4::kDirectK) > 0x7FFFFFFF)
             return DQ4_EUNSUPPORTED;
-        const bool full = plan.direct && dq4::direct_split_fits(rps, n_cols, ld_src1,
-                                                                 plan.tile_i, transposed);
+        const bool full = plan.direct && dq4::direct_split_fits(rps, n_cols, r_ld[k],
+                                                                 plan.tile_i, r_tr[k]);
         float *r_dst = dst + r.i_begin * n_cols;
-        const float *r_src1 = transposed ? src1 + r.i_begin * ld_src1 : src1 + r.i_begin;
-        launches[k] = {{packed, scale_codes, nested_absmax, scale_codebook, codebook4, r_src1,
-                        splits > 1 ? workspace : r_dst, n_rows, n_cols, r.m, ld_src1, rps,
+        launches[k] = {{packed, scale_codes, nested_absmax, scale_codebook, codebook4, r_src[k],
+                        splits > 1 ? workspace : r_dst, n_rows, n_cols, r.m, r_ld[k], rps,
                         offset, log2_block, static_cast<int>(tiles_i),
                         static_cast<int>(tiles_j), full ? 1 : 0},
                        groups, splits, r_count, r_dst};

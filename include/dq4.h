@@ -276,8 +276,18 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
  * the ranges reuse the workspace in turn.  The number of splits is the
  * largest of those the workspace holds up to the preferred count
  * (dq4_out_prod_fused_workspace_bytes); with workspace_bytes == 0 there is
- * one split and dst is written directly.  The workspace changes speed only;
- * the result is deterministic for a given device and workspace size.
+ * one split and dst is written directly.  A transposed src1 on the aligned
+ * path: the dst-row ranges whose tiles are 48 or 64 rows and at least 7/8
+ * used read a transposed src1 slowly, so when the workspace holds a
+ * row-major copy of those ranges' src1 columns (rounded up to 256 bytes)
+ * plus the partials of the resulting plan (dq4_out_prod_fused_workspace_bytes
+ * with src1_transposed = 1 is enough), the call first copies those columns
+ * to the start of the workspace (one more kernel) and those ranges run
+ * exactly as for a row-major src1, with the rest of the workspace; other
+ * ranges, or every range when the workspace is smaller, read src1 in place.
+ * With m == 1 both orientations are the same memory and take the row-major
+ * path.  The workspace changes speed only; the result is deterministic for a
+ * given device, orientation and workspace size.
  *
  * dst is overwritten (n_rows == 0 writes zeros); m == 0 or n_cols == 0 is a
  * no-op.  Everything is enqueued on `stream`; nothing is allocated or
@@ -296,10 +306,14 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
                                 int64_t workspace_bytes, void *stream);
 
 /* Workspace bytes at which dq4_out_prod_fused uses its preferred number of
- * row splits on the current device (0 when one split is preferred, or for
- * non-positive or oversized arguments).  Host only; queries the current
+ * row splits on the current device for a src1 of the given orientation (0
+ * when one split is preferred, or for non-positive or oversized arguments or
+ * a src1_transposed other than 0 or 1).  For a transposed src1 and
+ * n_cols % 8 == 0 this includes the row-major copy of src1 columns that
+ * dq4_out_prod_fused then makes (see there).  Host only; queries the current
  * device. */
-int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m);
+int64_t dq4_out_prod_fused_workspace_bytes(int64_t n_rows, int64_t n_cols, int64_t m,
+                                           int32_t src1_transposed);
 
 /*
  * Dequantize-plus-linear (bitsandbytes issue above, section "Problem": the

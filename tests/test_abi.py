@@ -159,7 +159,8 @@ def test_validation_out_prod_fused(lib):
     assert call(nested=128) == dq4.DQ4_EUNSUPPORTED
     # 256-row tiles at this m: 2^31 i-tiles, more than a grid can hold
     assert call(m=(1 << 31) * 256, ld=(1 << 31) * 256) == dq4.DQ4_EUNSUPPORTED
-    for args in ((0, 64, 8), (100, 0, 8), (100, 64, 0), (-1, 64, 8), (1 << 40, 1 << 40, 1 << 40)):
+    for args in ((0, 64, 8, 0), (100, 0, 8, 0), (100, 64, 0, 1), (-1, 64, 8, 0),
+                 (1 << 40, 1 << 40, 1 << 40, 0), (100, 64, 8, 2), (1 << 60, 64, 1 << 10, 1)):
         assert lib.dq4_out_prod_fused_workspace_bytes(*args) == 0
 
 

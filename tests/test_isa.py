@@ -48,7 +48,7 @@ def test_kernels_present(asm):
                           ("dq4_scale_codes_kernel", 1), ("dq4_add_offset_kernel", 1),
                           ("zero_fill_kernel", 1), ("int8_prep_kernel", 1),
                           ("out_prod_fused_kernel", 8), ("out_prod_direct_kernel", 28),
-                          ("out_prod_reduce_kernel", 1),
+                          ("out_prod_reduce_kernel", 1), ("src1_transpose_kernel", 1),
                           ("out_prod_zero_kernel", 1), ("dq4_memory_twin_kernel", 1),
                           ("dq4_shift_tile_kernel", 23)):
         assert sum(kernel in n for n in names) == count, kernel
@@ -64,6 +64,8 @@ def test_no_fused_or_packed_fp_instructions(asm):
         assert not found, f"{name}: {sorted(found)}"
         if "add_offset" in name or "reduce" in name:
             assert "v_add_f32" in code, name
+        elif "src1_transpose" in name:  # a bit copy of src1: no FP32 arithmetic at all
+            assert not re.search(r"\bv_(mul|add|sub|fma\w*|mac)_f32", code), name
         elif "zero_fill" not in name and "zero_kernel" not in name and "memory_twin" not in name:
             assert "v_mul_f32" in code, name
         if ("dq4_tile_kernel" in name or "dq4_elem_kernel" in name or "out_prod_fused" in name

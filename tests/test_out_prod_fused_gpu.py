@@ -215,6 +215,72 @@ def test_split_past_2_pow_32_weight_elements_keeps_the_checked_loads():
     torch.cuda.empty_cache()
 
 
+def _copied_rows(m):
+    """dst rows [0, n) whose src1 columns the call copies to row-major when
+    src1 is transposed and the workspace is the preferred one: the ranges
+    whose direct tile is 48 or 64 rows and at least 7/8 used (m > 64 is
+    whole 64-row tiles, then a rest with the smallest tile that holds it)."""
+    def tile(k):
+        return next(w for w in (1, 4, 8, 16, 32, 48, 64) if k <= w)
+
+    def pays(k):
+        return tile(k) >= 48 and 8 * k >= 7 * tile(k)
+
+    whole = m // 64 * 64 if m > 64 else 0
+    rest = m - whole
+    if whole and rest and pays(rest):
+        return m
+    if whole:
+        return whole
+    return m if pays(m) else 0
+
+
+@pytest.mark.parametrize("m", [1, 4, 33, 44, 64, 150, 192])
+def test_transposed_src1_copy_path_equals_the_row_major_call(m):
+    """A transposed src1 with the preferred workspace for that orientation:
+    the dst-row ranges with wide, nearly full tiles copy their src1 columns
+    to a row-major matrix in the workspace and then sum exactly as a
+    row-major src1 does with the row-major preferred workspace, so those dst
+    rows must carry the same bits as the row-major call's.  The src1 rows
+    are padded (ld > n_rows) so the copy reads through the leading
+    dimension.  The other rows, and every row with an empty workspace, read
+    src1 in place, within the FP32 summation bound of the oracle's weight
+    times src1.  At m = 1 both orientations are the same memory and give the
+    same bits."""
+    n_rows, n_cols = 4099, 256
+    x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=m + 4242, n_rows=n_rows,
+                           n_cols=n_cols)
+    dev = dq4.to_device(x)
+    rng = np.random.Generator(np.random.PCG64(m + 17))
+    b = rng.standard_normal((n_rows, m)).astype(np.float32)
+    kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64)
+    p_row = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    p_tr = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m, src1_transposed=True)
+    copied = _copied_rows(m)
+    assert p_tr >= n_rows * copied * 4
+    if m == 1:
+        assert p_tr == p_row
+    row = torch.from_numpy(b).cuda()
+    padded = torch.full((m, n_rows + 13), float("nan"), device="cuda")
+    padded[:, :n_rows] = torch.from_numpy(np.ascontiguousarray(b.T)).cuda()
+    tr = padded[:, :n_rows]                                   # ld = n_rows + 13
+    y_row = dq4.dq4_out_prod_fused(**dev, **kw, src1=row, workspace=torch.empty(
+        max(p_row // 4, 0), device="cuda")).cpu().numpy()
+    y_tr = dq4.dq4_out_prod_fused(**dev, **kw, src1=tr, src1_transposed=True,
+                                  workspace=torch.empty(p_tr // 4, device="cuda")).cpu().numpy()
+    same = m if m == 1 else copied
+    assert np.array_equal(y_tr[:same].view(np.uint32), y_row[:same].view(np.uint32)), f"m={m}"
+    y_direct = dq4.dq4_out_prod_fused(**dev, **kw, src1=tr, src1_transposed=True,
+                                      workspace=torch.empty(0, device="cuda")).cpu().numpy()
+    exact, mag = out_prod_reference(x, n_rows, n_cols, b)
+    check_sum_bound(y_direct, exact, mag, n_rows, f"transposed in place, m={m}")
+    check_sum_bound(y_tr, exact, mag, n_rows, f"transposed, preferred workspace, m={m}")
+    if m == 1:
+        y_row0 = dq4.dq4_out_prod_fused(**dev, **kw, src1=row,
+                                        workspace=torch.empty(0, device="cuda")).cpu().numpy()
+        assert np.array_equal(y_direct.view(np.uint32), y_row0.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [1, 4, 16, 64])
 def test_split_of_2_pow_31_steps_is_refused_before_any_launch(m):
     """The kernels count a split's 4-row steps in 32 bits.  With no workspace
