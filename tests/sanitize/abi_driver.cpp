@@ -36,7 +36,9 @@ int main()
     expect(dq4_out_prod_fused(p8, p8, pf, pf, pf, 0.f, 10, 64, 64, 256, pf, 4, 3, 0, pf, nullptr, 0, nullptr), DQ4_EINVAL, "fused ld < m");
     expect(dq4_out_prod_fused(p8, p8, pf, pf, pf, 0.f, 10, 64, 64, 256, pf, 0, 4, 0, pf, nullptr, 0, nullptr), DQ4_OK, "fused m=0");
     expect(dq4_out_prod_fused(p8, p8, pf, pf, pf, 0.f, 10, 64, 64, 256, pf, 4, 4, 0, pf, nullptr, 64, nullptr), DQ4_EINVAL, "fused size without workspace");
-    expect(static_cast<int>(dq4_out_prod_fused_workspace_bytes(INT64_MAX, INT64_MAX, 2)), 0, "fused workspace overflow");
+    expect(static_cast<int>(dq4_out_prod_fused_workspace_bytes(INT64_MAX, INT64_MAX, 2, 0)), 0, "fused workspace overflow");
+    expect(static_cast<int>(dq4_out_prod_fused_workspace_bytes(INT64_MAX, 64, 2, 1)), 0, "fused workspace copy overflow");
+    expect(static_cast<int>(dq4_out_prod_fused_workspace_bytes(100, 64, 8, 2)), 0, "fused workspace orientation");
     expect(dq4_dequant_linear(p8, p8, pf, pf, pf, 0.f, 64, 64, 64, 256, DQ4_F32, 0, pv, 4, pv, pv, nullptr), DQ4_EINVAL, "linear f32");
     expect(dq4_int8_prep(nullptr, 4, 64, nullptr, nullptr, 8, nullptr, 0, nullptr, nullptr, nullptr), DQ4_OK, "int8 L=0");
     expect(dq4_int8_prep(reinterpret_cast<uint16_t *>(pv), 1 << 20, 1 << 12, reinterpret_cast<int8_t *>(pv), pf, 8,
