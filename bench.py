@@ -453,16 +453,20 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
     m = args.out_prod_m
     g = torch.Generator(device="cuda:0").manual_seed(7)
     src1 = torch.randn((wl.n_rows, m), dtype=torch.float32, device="cuda:0", generator=g)
+    # with --out-prod-transposed the routes get the same values stored m x n_rows
+    transposed = bool(args.out_prod_transposed)
+    src1_arg = src1.t().contiguous() if transposed else src1
     dst = torch.empty((m, wl.n_cols), dtype=torch.float32, device="cuda:0")
     budget = 256 << 20
     rows_pb = dq4.dq4_rows_per_block(wl.n_cols, 4, budget)
     ws = torch.empty(rows_pb * wl.n_cols, dtype=torch.float32, device="cuda:0")
     windows = dq4.dq4_row_windows(wl.n_rows, wl.n_cols, 4, budget)
     flops = 2.0 * m * wl.n_rows * wl.n_cols
-    fused_ws_bytes = dq4.dq4_out_prod_fused_workspace_bytes(wl.n_rows, wl.n_cols, m)
+    fused_ws_bytes = dq4.dq4_out_prod_fused_workspace_bytes(wl.n_rows, wl.n_cols, m,
+                                                            src1_transposed=transposed)
     fused_ws = torch.empty(max(fused_ws_bytes // 4, 0), dtype=torch.float32, device="cuda:0")
     kw = dict(offset=float(x.offset), n_rows=wl.n_rows, n_cols=wl.n_cols, blocksize=64,
-              src1=src1)
+              src1=src1_arg, src1_transposed=transposed)
 
     def timeit(fn, reps):
         # each route is warmed on its own before it is timed: at least 20
@@ -521,7 +525,9 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
         rows_s = rows_pb
         dst_s = torch.empty((m, wl.n_cols), dtype=torch.float32, device="cuda:0")
         dq4.dq4_out_prod_fused(**dev, offset=float(x.offset), n_rows=rows_s, n_cols=wl.n_cols,
-                               blocksize=64, src1=src1[:rows_s], dst=dst_s)
+                               blocksize=64,
+                               src1=src1_arg[:, :rows_s] if transposed else src1[:rows_s],
+                               src1_transposed=transposed, dst=dst_s)
         got_s = dst_s.cpu().numpy().astype(np.float64)
         a_s = src1[:rows_s].cpu().numpy().astype(np.float64)
         w_s, t_deq = oracle_dequant_threaded(x, 0, rows_s * wl.n_cols, "f32", host_threads())
@@ -545,7 +551,8 @@ def out_prod_bench(args, torch, dq4, inputs) -> int:
         "metric": "out_prod of the 151936x5376 NF4 output head, FP32 TFLOP/s (fused route)",
         "value": tflops["fused"], "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
         "data": "synthetic",
-        "config": {"workload": wl.name, "m": m, "windows": len(windows),
+        "config": {"workload": wl.name, "m": m, "src1_transposed": transposed,
+                   "windows": len(windows),
                    "rows_per_window": rows_pb, "transient_bytes": rows_pb * wl.n_cols * 4,
                    "fused_workspace_bytes": fused_ws_bytes},
         "ms_fused": round(t_fused, 4), "ms_blocked": round(t_blocked, 4),
@@ -1090,6 +1097,8 @@ def main() -> int:
                          "151936x5376 output head (FP32 GEMM per window)")
     ap.add_argument("--out-prod-m", type=int, default=512,
                     help="columns of src1 (tokens) for --out-prod")
+    ap.add_argument("--out-prod-transposed", action="store_true",
+                    help="--out-prod: src1 stored transposed (m x n_rows) for both routes")
     ap.add_argument("--linear", action="store_true",
                     help="instead of the benchmark, time dequantize-plus-linear forward and "
                          "grad_A cells")

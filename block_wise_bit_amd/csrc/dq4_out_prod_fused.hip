@@ -1053,19 +1053,31 @@ __global__ __launch_bounds__(kThreads) void src1_transpose_kernel(const float *s
     const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kTrTile;
     const int nr = static_cast<int>(min(int64_t{kTrTile}, n_rows - r0));
     const int ni = static_cast<int>(min(int64_t{kTrTile}, m - i0));
-    for (int k = t; k < kTrTile * kTrTile; k += kThreads) {
+    // every lane's 16 loads are issued before any is stored (a loop that
+    // stored each load before the next ran the copy at about 3 TB/s)
+    constexpr int kPer = kTrTile * kTrTile / kThreads;
+    float v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int k = t + q * kThreads;
         const int ii = k / kTrTile, rr = k % kTrTile;
-        if (ii < ni && rr < nr)
-            tile[ii][rr] = src1[(i0 + ii) * ld + r0 + rr];
+        v[q] = ii < ni && rr < nr ? src1[(i0 + ii) * ld + r0 + rr] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int k = t + q * kThreads;
+        tile[k / kTrTile][k % kTrTile] = v[q];
     }
     __syncthreads();
     // lanes step through the tile's rows in runs of the next power of two
     // of ni (shifts, not a division: the compiler expands a 32-bit division
-    // into floating-point instructions)
+    // into floating-point instructions); nr << lg <= 64 * 64
     const int lg = 32 - __clz(ni - 1);  // ni >= 1; ni == 1 gives 0
-    for (int k = t; k < (nr << lg); k += kThreads) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int k = t + q * kThreads;
         const int rr = k >> lg, ii = k & ((1 << lg) - 1);
-        if (ii < ni)
+        if (rr < nr && ii < ni)
             out[(r0 + rr) * m + i0 + ii] = tile[ii][rr];
     }
 }
@@ -1284,17 +1296,16 @@ int64_t src1_copy_bytes(int64_t n_rows, int64_t cols)
 
 // A transposed src1 in the 48- and 64-row direct tiles reads 16 lines per
 // load where a row-major one reads 4, and a row-major copy of the range's
-// columns pays for itself once such a tile is at least 7/8 full.  Measured
-// on the output head against the in-place read: m = 44 .. 48 and 60 .. 64
-// 2-6 % faster with the copy, m = 52 and 56 within 1 %, m = 33 .. 40 (a
-// sparse 48-row tile, whose unused lanes share lines) 1-2 % slower; whole
-// 64-row ranges 2-6 % faster; and a 1-row rest range 0.4-0.6 % slower
-// reading a wide copy than reading src1 in place.  The narrower tiles (4-row
-// sets, and the 16- and 32-row tiles with their super-steps) were within
-// 1 % either way.
+// columns pays for itself in every 64-row range and in a 48-row one with at
+// least 40 rows.  Measured on the output head against the in-place read:
+// m = 44 .. 64 and whole 64-row ranges 1.4-7 % faster with the copy (m = 50
+// .. 54, a 64-row tile at 3/4 use, 1.4-1.7 %), m = 40 .. 42 within 1 %, and
+// m = 33 .. 36 (a sparse 48-row tile, whose unused lanes share lines with
+// the used ones) 0.5 % slower.  The narrower tiles (4-row sets, and the 16-
+// and 32-row tiles with their super-steps) were within 1 % either way.
 bool copy_pays(const RowRange &r)
 {
-    return r.plan.direct && r.plan.tile_i >= 48 && r.m * 8 >= int64_t{r.plan.tile_i} * 7;
+    return r.plan.direct && (r.plan.tile_i == 64 || (r.plan.tile_i == 48 && r.m >= 40));
 }
 
 // For a transposed src1 on the aligned path: marks the ranges whose columns

@@ -277,8 +277,8 @@ dq4_status_t dq4_out_prod_rows(const uint8_t *packed, const uint8_t *scale_codes
  * largest of those the workspace holds up to the preferred count
  * (dq4_out_prod_fused_workspace_bytes); with workspace_bytes == 0 there is
  * one split and dst is written directly.  A transposed src1 on the aligned
- * path: the dst-row ranges whose tiles are 48 or 64 rows and at least 7/8
- * used read a transposed src1 slowly, so when the workspace holds a
+ * path: the dst-row ranges whose tiles are 64 rows, or 48 rows with at
+ * least 40 used, read a transposed src1 slowly, so when the workspace holds a
  * row-major copy of those ranges' src1 columns (rounded up to 256 bytes)
  * plus the partials of the resulting plan (dq4_out_prod_fused_workspace_bytes
  * with src1_transposed = 1 is enough), the call first copies those columns

@@ -218,13 +218,14 @@ def test_split_past_2_pow_32_weight_elements_keeps_the_checked_loads():
 def _copied_rows(m):
     """dst rows [0, n) whose src1 columns the call copies to row-major when
     src1 is transposed and the workspace is the preferred one: the ranges
-    whose direct tile is 48 or 64 rows and at least 7/8 used (m > 64 is
-    whole 64-row tiles, then a rest with the smallest tile that holds it)."""
+    whose direct tile is 64 rows, or 48 rows with at least 40 of them used
+    (m > 64 is whole 64-row tiles, then a rest with the smallest tile that
+    holds it)."""
     def tile(k):
         return next(w for w in (1, 4, 8, 16, 32, 48, 64) if k <= w)
 
     def pays(k):
-        return tile(k) >= 48 and 8 * k >= 7 * tile(k)
+        return tile(k) == 64 or (tile(k) == 48 and k >= 40)
 
     whole = m // 64 * 64 if m > 64 else 0
     rest = m - whole
@@ -235,10 +236,10 @@ def _copied_rows(m):
     return m if pays(m) else 0
 
 
-@pytest.mark.parametrize("m", [1, 4, 33, 44, 64, 150, 192])
+@pytest.mark.parametrize("m", [1, 4, 33, 44, 52, 64, 97, 150, 192])
 def test_transposed_src1_copy_path_equals_the_row_major_call(m):
     """A transposed src1 with the preferred workspace for that orientation:
-    the dst-row ranges with wide, nearly full tiles copy their src1 columns
+    the dst-row ranges with wide, well-used tiles copy their src1 columns
     to a row-major matrix in the workspace and then sum exactly as a
     row-major src1 does with the row-major preferred workspace, so those dst
     rows must carry the same bits as the row-major call's.  The src1 rows
