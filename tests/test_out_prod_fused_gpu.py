@@ -579,25 +579,30 @@ def test_edge_cases():
                                                                 device="cuda"))
 
 
-@pytest.mark.parametrize("m", [1, 4, 32])
-def test_graph_capture_replays_with_splits(m):
+@pytest.mark.parametrize("m,transposed", [(1, False), (4, False), (32, False), (33, True),
+                                           (64, True)])
+def test_graph_capture_replays_with_splits(m, transposed):
     """The fused route -- kernel plus the reduction over row splits -- captured
     in a HIP graph and replayed several times, with new src1 values written
     eagerly between replays: every replay equals an eager call on the same
     src1 bit for bit (the result is deterministic for a given workspace).
     m = 1 takes the vector-unit row, m = 4 the 4-row set, m = 32 the 32-row
-    tile."""
+    tile; a transposed src1 at m = 33 is read in place by the 48-row tile, and
+    at m = 64 copied to row-major in the workspace first (one more kernel in
+    the graph)."""
     n_rows, n_cols = 20000, 384
     x = inputs.make_inputs(n_rows * n_cols, 64, "nf4", 0.03, seed=20000, n_rows=n_rows,
                            n_cols=n_cols)
     dev = dq4.to_device(x)
-    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m)
+    preferred = dq4.dq4_out_prod_fused_workspace_bytes(n_rows, n_cols, m,
+                                                       src1_transposed=transposed)
     assert preferred > 0, "this shape should split its rows"
     ws = torch.empty(preferred // 4, dtype=torch.float32, device="cuda")
-    src1 = torch.empty((n_rows, m), dtype=torch.float32, device="cuda")
+    src1 = torch.empty((m, n_rows) if transposed else (n_rows, m), dtype=torch.float32,
+                       device="cuda")
     dst = torch.empty((m, n_cols), dtype=torch.float32, device="cuda")
     kw = dict(offset=float(x.offset), n_rows=n_rows, n_cols=n_cols, blocksize=64, src1=src1,
-              workspace=ws)
+              src1_transposed=transposed, workspace=ws)
     g_rand = torch.Generator(device="cuda").manual_seed(11)
     src1.normal_(generator=g_rand)
     side = torch.cuda.Stream()
