@@ -1198,11 +1198,14 @@ def main() -> int:
     achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
     print(f"[bench] {K} timed steps: {ms_per_step * 1e3:.2f} us/step wall, "
           f"{kernel_us:.2f} us/launch (events)", file=sys.stderr, flush=True)
-    last_out = sets[(K - 1) % len(sets)][1].cpu()
 
     # the spread: the same K steps again, right after the timed region, in
     # `batches` batches with an event pair each
     batch_us = timed_batches(step, per, stream, torch, first=K)
+    # the timed region's last output, for the parity check: the batches wrote
+    # the same bits into it again (the call is deterministic), and the copy
+    # waits until now so that the GPU does not idle before the batches
+    last_out = sets[(K - 1) % len(sets)][1].cpu()
 
     # the memory twin, timed the same way on the same buffer sets: the same
     # tiles, loads and stores with no arithmetic -- the ceiling of this access
