@@ -1448,7 +1448,9 @@ dq4_status_t dq4_out_prod_fused(const uint8_t *packed, const uint8_t *scale_code
         // partials of the plan that reads it: one more kernel writes the copy
         // at the start of the workspace, and those ranges run as for a
         // row-major src1 on it, with the rest of the workspace.
-        dq4::RowRange planned[2] = {ranges[0], ranges[1]};
+        dq4::RowRange planned[2];
+        for (int k = 0; k < n_ranges; ++k)
+            planned[k] = ranges[k];
         bool copied[2];
         int64_t c0 = 0, c1 = 0;
         const int64_t copy_bytes = dq4::plan_copy(n_rows, m, whole_blocks, planned, n_ranges,
