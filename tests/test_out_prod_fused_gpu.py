@@ -236,7 +236,7 @@ def _copied_rows(m):
     return m if pays(m) else 0
 
 
-@pytest.mark.parametrize("m", [1, 4, 33, 44, 52, 64, 97, 150, 192])
+@pytest.mark.parametrize("m", [1, 4, 33, 44, 52, 64, 97, 116, 150, 192])
 def test_transposed_src1_copy_path_equals_the_row_major_call(m):
     """A transposed src1 with the preferred workspace for that orientation:
     the dst-row ranges with wide, well-used tiles copy their src1 columns
